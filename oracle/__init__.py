@@ -1,0 +1,33 @@
+"""CPU oracle for the KIVI grouped KV-cache codec.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links
+anything in this package; only the test-suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` use it.
+
+Two tiers, written independently of each other and of the HIP path:
+
+* :mod:`oracle.kivi_ref`   -- vectorised numpy in explicit float32/float16.
+* :mod:`oracle.kivi_exact` -- pure Python on exact rationals with a
+  hand-written round-to-nearest-even into the binary16/binary32 formats,
+  for tiny inputs.  It pins the numpy tier's use of hardware rounding.
+
+Sources (titles of the pages the method is taken from):
+
+* CacheForge README, "How it works": keys are quantized per channel, values
+  per token, the most recent tokens are kept at higher precision; the
+  "Example" section names the knobs ``k_bits``, ``v_bits``, ``group_size``
+  and ``residual_length`` (recent fp16 tokens), defaults 2/2/32/128.
+* CacheSeek pull request #4 "Feature(quantization): add KIVI KV-cache
+  quantization for exact-prefix reuse", description: KIVI encode/decode with
+  grouped statistics, padding, and packing of the codes into int32 words;
+  compact ``qdata``/``scale``/``offset`` payload.
+* vLLM ``turboquant/config.py``, ``TurboQuantConfig`` docstring ("3 = 8
+  levels, 4 = 16 levels": b bits give 2**b levels) and ``value_packed_size``
+  (a per-vector uniform value code costs ceil(D*b/8) bytes plus an fp16
+  scale and an fp16 zero).
+
+The pages print no formula for the statistics or the rounding; the readings
+used here are stated in each function's docstring.
+"""
+
+from . import kivi_ref, kivi_exact  # noqa: F401
