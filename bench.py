@@ -1,0 +1,220 @@
+"""Benchmark of the KIVI KV-cache codec on one MI355X.
+
+One step = the whole full-cache hot path over one synthetic cache: per-channel
+key encode, per-token value encode, key decode, value decode, each as one
+call over every (layer, batch, head) slice, with the residual window of R
+recent tokens left in fp16.  Inputs are generated on the GPU before timing.
+
+Prints one JSON line.  ``value`` is the fp16-equivalent encode+decode
+throughput: (fp16 bytes of K and V consumed by encode + produced by decode)
+per second.  ``roofline`` is for the kernel with the largest share of the
+step, from HIP events on the stream the kernels run on; ``cpu_baseline`` is
+the numpy oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, 8 TB/s
+
+
+def algorithmic_bytes(kind: str, direction: str, S: int, n: int, D: int, G: int, b: int) -> int:
+    """Bytes one launch must move: fp16 data plus packed codes plus fp16 sidecars
+    (padding slots included, since they are written/read)."""
+    fp16 = S * n * D * 2
+    if kind == "k":
+        ng = -(-n // G)
+        codes = S * ng * (G * b // 32) * D * 4
+        stats = 2 * S * ng * D * 2
+    else:
+        ngv = -(-D // G)
+        codes = S * n * ngv * (G * b // 32) * 4
+        stats = 2 * S * n * ngv * 2
+    return fp16 + codes + stats
+
+
+def kernel_source_hash() -> str:
+    path = os.path.join(ROOT, "kv_cache_quantization_codec_amd", "csrc", "kivi_kernels.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters for this kernel
+    source, read from profiles/traffic_<workload>.json (None when absent or
+    taken on another version of the kernels)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch", {}).get(kernel)
+
+
+def cpu_baseline(k, v, w, cfg, n, budget_s=12.0):
+    """Time the numpy oracle (single thread) on whole slices of the same cache
+    until about ``budget_s`` seconds of CPU work; scale to fp16-eq GB/s."""
+    import numpy as np
+
+    from oracle import kivi_ref as ref
+
+    G = cfg.group_size
+    done = 0
+    spent = 0.0
+    S = k.shape[0]
+    chunk = 8
+    while spent < budget_s and done < S:
+        sl = slice(done, min(done + chunk, S))
+        kh = k[sl].cpu().numpy()
+        vh = v[sl].cpu().numpy()
+        t0 = time.perf_counter()
+        kc, ks, kz = ref.encode_k(kh, n, cfg.k_bits, G)
+        vc, vs, vz = ref.encode_v(vh, n, cfg.v_bits, G)
+        ref.decode_k(kc, ks, kz, n, cfg.k_bits, G)
+        ref.decode_v(vc, vs, vz, n, cfg.v_bits, G, cfg.head_dim)
+        spent += time.perf_counter() - t0
+        done = sl.stop
+    fp16_bytes = 2 * 2 * done * n * cfg.head_dim * 2
+    return {
+        "value": round(fp16_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {S} slices ({done * n} tokens x {cfg.head_dim} channels, K and V), "
+                  f"numpy oracle encode+decode, {spent:.1f} s single-threaded "
+                  f"(host has {len(os.sched_getaffinity(0))} cores available)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2_7b_2bit",
+                    choices=["llama2_7b_2bit", "mistral_7b_k2v4", "single_layer_4bit"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this codec benchmark runs on one GPU only; "
+                                   "--gpus must be 1 (slices shard across GPUs with no exchange, "
+                                   "so per-GPU throughput is the figure)"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_quantization_codec_amd as K
+    from kvsynth import WORKLOADS, layer_kv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K.binding.lib()
+    w = WORKLOADS[args.workload]
+    cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
+    S, T, D, G = w.slices, w.tokens, w.head_dim, w.group_size
+    n = T - w.residual_length
+    dev = torch.device("cuda:0")
+
+    k = torch.empty((S, T, D), dtype=torch.float16, device=dev)
+    v = torch.empty_like(k)
+    spl = w.slices_per_layer
+    for layer in range(w.layers):
+        kl, vl = layer_kv(w, layer, device=dev)
+        k[layer * spl:(layer + 1) * spl] = kl
+        v[layer * spl:(layer + 1) * spl] = vl
+        del kl, vl
+    kq = K.alloc_keys(cfg, S, n, dev)
+    vq = K.alloc_values(cfg, S, n, dev)
+    ko = torch.empty((S, n, D), dtype=torch.float16, device=dev)
+    vo = torch.empty_like(ko)
+    torch.cuda.synchronize()
+
+    names = ["encode_k", "encode_v", "decode_k", "decode_v"]
+    calls = [
+        lambda: K.kivi_encode_k(cfg, k, n, *kq),
+        lambda: K.kivi_encode_v(cfg, v, n, *vq),
+        lambda: K.kivi_decode_k(cfg, *kq, n, ko),
+        lambda: K.kivi_decode_v(cfg, *vq, n, vo),
+    ]
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        for j, c in enumerate(calls):
+            c()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1000.0 / args.steps
+    per_kernel_ms = {nm: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / args.steps
+                     for j, nm in enumerate(names)}
+
+    fp16_eq = 2 * 2 * S * n * D * 2                  # K and V, encode + decode
+    bits = {"encode_k": w.k_bits, "decode_k": w.k_bits, "encode_v": w.v_bits, "decode_v": w.v_bits}
+    alg = {nm: algorithmic_bytes(nm[-1], nm[:6], S, n, D, G, bits[nm]) for nm in names}
+    moved = sum(alg.values())
+    dom = max(names, key=lambda nm: per_kernel_ms[nm])
+    achieved = alg[dom] / (per_kernel_ms[dom] / 1000.0) / 1e9
+    traffic = measured_traffic(dom, args.workload)
+    tokens = w.batch * n                              # sequence positions, all layers and heads
+
+    out = {
+        "metric": "KV encode+decode GB/s (fp16-equivalent) and % of HBM roofline, 1 MI355X",
+        "value": round(fp16_eq / (ms_step / 1000.0) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "layers": w.layers, "batch": w.batch, "kv_heads": w.heads, "head_dim": D,
+            "seq_len": T, "quantized_tokens": n, "residual_length": w.residual_length,
+            "k_bits": w.k_bits, "v_bits": w.v_bits, "group_size": G,
+        },
+        "moved_GBps": round(moved / (ms_step / 1000.0) / 1e9, 2),
+        "hbm_roofline_frac_step": round(moved / (ms_step / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(tokens / (ms_step / 1000.0), 1),
+        "kernel_ms": {nm: round(x, 4) for nm, x in per_kernel_ms.items()},
+        "kernel_GBps": {nm: round(alg[nm] / (per_kernel_ms[nm] / 1000.0) / 1e9, 1) for nm in names},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg[dom],
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(k, v, w, cfg, n, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+/*
+ * kivi.h -- C ABI of libkivi, the KIVI grouped KV-cache codec for AMD
+ * MI355X (gfx950).
+ *
+ * Method.  CacheForge README, "How it works": keys are quantized per
+ * channel, values per token, and the most recent tokens stay in higher
+ * precision; its "Example" section names the four knobs k_bits, v_bits,
+ * group_size and residual_length (the count of recent tokens kept fp16).
+ * CacheSeek pull request #4 ("Feature(quantization): add KIVI KV-cache
+ * quantization for exact-prefix reuse"), description: KIVI encode/decode
+ * with grouped statistics, padding of partial groups, codes packed into
+ * int32 words, and a compact qdata/scale/offset payload that is produced
+ * on the tensor's own device.
+ *
+ * The pages print no formula; this library implements the reading
+ *   per group:  mn, mx     = min, max of the group's valid fp16 elements
+ *                            (a negative zero counts as +0)
+ *               scale      = fp16( fp32( fp32(mx - mn) / (2^b - 1) ) )
+ *               zero       = mn                              (exact in fp16)
+ *   per element: q         = clamp( rint( fp32( fp32(x - zero) / scale ) ),
+ *                                   0, 2^b - 1 )   (IEEE division, rint
+ *                                                   = round half to even;
+ *                                                   q = 0 when scale == 0)
+ *   decode:     xhat       = fp16( fp32( q * scale + zero ) )
+ * with every rounding to nearest, ties to even.  Code i of a 32-bit word
+ * sits at bits [i*b, i*b + b); word w of a group holds the group's
+ * elements w*(32/b) .. w*(32/b) + 32/b - 1.  Padding slots hold code 0.
+ *
+ * Terms used below.
+ *   slice    one independent (layer, batch, head) sequence of a KV cache.
+ *   D        head_dim.  G = group_size.  b = k_bits or v_bits.
+ *   W        = G*b/32, int32 words per group.
+ *   NG_k(n)  = ceil(n / G), key groups of n tokens (last one padded).
+ *   NG_v     = ceil(D / G), value groups of one token (last one padded).
+ *
+ * Layouts (row-major, innermost last; fp16 data is passed as raw 16-bit
+ * patterns through void pointers):
+ *   K or V input   fp16  [n_slices][in_slice_stride]; token t of slice s
+ *                        starts at element s*in_slice_stride + t*D.
+ *   key codes      int32 [n_slices][NG_k(cap_tokens)*W][D]   (channel innermost)
+ *   key scale/zero fp16  [n_slices][NG_k(cap_tokens)][D]
+ *   value codes    int32 [n_slices][cap_tokens][NG_v*W]
+ *   value scale/zero fp16 [n_slices][cap_tokens][NG_v]
+ *   decoded K or V fp16  [n_slices][out_slice_stride]; token t of slice s
+ *                        starts at element s*out_slice_stride + t*D.
+ *
+ * Ownership and execution.  The caller allocates and frees every buffer
+ * (device memory for all array arguments; host memory for kivi_config and
+ * kivi_stream).  The library never allocates, frees or synchronises: each
+ * call only validates its arguments on the host and enqueues kernels on
+ * hip_stream (a hipStream_t; NULL means the default stream), so outputs are
+ * ready when that stream reaches the enqueued work.  Calls on different
+ * streams are independent and re-entrant; the library's only global state
+ * is the thread-local code of the last failed HIP launch.
+ *
+ * Errors.  Every entry point returns KIVI_OK (0) or a negative KIVI_E_*
+ * code.  Argument checks all run before any HIP call, so a non-zero return
+ * other than KIVI_E_HIP means that nothing was enqueued and no output (and
+ * no kivi_stream field) was touched.  Nothing aborts and no C++ exception
+ * crosses the ABI.  Array pointers must be 16-byte aligned and slice
+ * strides multiples of 8 elements.  Calls with n_slices == 0 or
+ * n_tokens == 0 validate the configuration and return KIVI_OK without
+ * touching any pointer.
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Codec configuration (CacheForge README, "Example": k_bits, v_bits,
+ * group_size, residual_length; vLLM turboquant/config.py, TurboQuantConfig:
+ * head_dim, e.g. 64, 96, 128).
+ *   k_bits, v_bits   2, 4 or 8, independently.
+ *   group_size       32, 64 or 128; shared by keys (tokens per key group)
+ *                    and values (channels per value group).
+ *   residual_length  R >= 0: the most recent R tokens stay fp16.
+ *   head_dim         D, a multiple of 8 in [8, 256]. */
+typedef struct kivi_config {
+    int32_t k_bits;
+    int32_t v_bits;
+    int32_t group_size;
+    int32_t residual_length;
+    int32_t head_dim;
+} kivi_config;
+
+enum {
+    KIVI_OK = 0,
+    KIVI_E_NULL = -1,       /* a required pointer is NULL */
+    KIVI_E_BITS = -2,       /* k_bits or v_bits not in {2, 4, 8} */
+    KIVI_E_GROUP = -3,      /* group_size not in {32, 64, 128} */
+    KIVI_E_HEAD_DIM = -4,   /* head_dim not a multiple of 8 in [8, 256] */
+    KIVI_E_RESIDUAL = -5,   /* residual_length < 0 */
+    KIVI_E_SHAPE = -6,      /* negative count, stride < n_tokens*D, cap_tokens < n_tokens, size overflow */
+    KIVI_E_ALIGN = -7,      /* pointer not 16-byte aligned or stride not a multiple of 8 */
+    KIVI_E_CAPACITY = -8,   /* streaming flush would pass cap_tokens */
+    KIVI_E_STATE = -9,      /* kivi_stream counters inconsistent */
+    KIVI_E_HIP = -10        /* a HIP launch failed; see kivi_last_hip_error() */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kivi_status_string(int status);
+
+/* hipError_t of the last failed launch on the calling thread (0 if none). */
+int kivi_last_hip_error(void);
+
+/* Checks a configuration; returns KIVI_OK or the matching KIVI_E_* code. */
+int kivi_validate_config(const kivi_config* cfg);
+
+/* Sizes per slice, for a capacity of n_tokens quantized tokens (CacheSeek
+ * PR #4: the manager accounts the stored payload size itself).  Return -1
+ * for an invalid configuration or n_tokens < 0.
+ *   kivi_k_code_words  int32 words of key codes     = NG_k(n)*W_k*D
+ *   kivi_k_stat_elems  fp16 elements of ONE key sidecar (scale or zero)
+ *                                                   = NG_k(n)*D
+ *   kivi_v_code_words  int32 words of value codes   = n*NG_v*W_v
+ *   kivi_v_stat_elems  fp16 elements of ONE value sidecar = n*NG_v
+ *   kivi_ring_elems    fp16 elements of one residual ring (keys or values)
+ *                      of the streaming state       = (R + G)*D          */
+int64_t kivi_k_code_words(const kivi_config* cfg, int64_t n_tokens);
+int64_t kivi_k_stat_elems(const kivi_config* cfg, int64_t n_tokens);
+int64_t kivi_v_code_words(const kivi_config* cfg, int64_t n_tokens);
+int64_t kivi_v_stat_elems(const kivi_config* cfg, int64_t n_tokens);
+int64_t kivi_ring_elems(const kivi_config* cfg);
+
+/* Per-channel key quantization (CacheForge README, "How it works": keys
+ * per channel; CacheSeek PR #4: grouped stats, padding, int32 packing).
+ * Quantizes tokens [0, n_tokens) of every slice of k_fp16 in groups of G
+ * tokens per channel; the last group of a slice may be partial, its
+ * statistics use only the valid tokens and its pad slots get code 0.  The
+ * caller passes n_tokens = T - R to keep the R most recent of T tokens in
+ * fp16 (those are not read).  Writes, per slice, key groups [0, NG_k(n))
+ * of codes/scale/zero, laid out for a capacity of cap_tokens >= n_tokens
+ * tokens (pass cap_tokens = n_tokens for dense output); groups beyond
+ * NG_k(n) are not touched. */
+int kivi_encode_k(const kivi_config* cfg, const void* k_fp16,
+                  int64_t n_slices, int64_t n_tokens, int64_t in_slice_stride,
+                  int64_t cap_tokens, int32_t* codes,
+                  void* scale_fp16, void* zero_fp16, void* hip_stream);
+
+/* Per-token value quantization (CacheForge README, "How it works": values
+ * per token).  Quantizes rows [0, n_tokens) of every slice in groups of G
+ * channels; when D is not a multiple of G the last group is padded.  Writes
+ * value rows [0, n_tokens) of the cap_tokens-row layouts. */
+int kivi_encode_v(const kivi_config* cfg, const void* v_fp16,
+                  int64_t n_slices, int64_t n_tokens, int64_t in_slice_stride,
+                  int64_t cap_tokens, int32_t* codes,
+                  void* scale_fp16, void* zero_fp16, void* hip_stream);
+
+/* Unpack and dequantize keys (CacheSeek PR #4: decoding moves only the
+ * compact qdata/scale/offset to the target device before dequantization).
+ * Reads key groups [0, NG_k(n_tokens)) of a cap_tokens layout and writes
+ * exactly n_tokens*D fp16 values per slice to out_fp16 (never a pad slot). */
+int kivi_decode_k(const kivi_config* cfg, const int32_t* codes,
+                  const void* scale_fp16, const void* zero_fp16,
+                  int64_t n_slices, int64_t n_tokens, int64_t cap_tokens,
+                  void* out_fp16, int64_t out_slice_stride, void* hip_stream);
+
+/* Unpack and dequantize values; same contract as kivi_decode_k for value
+ * rows [0, n_tokens). */
+int kivi_decode_v(const kivi_config* cfg, const int32_t* codes,
+                  const void* scale_fp16, const void* zero_fp16,
+                  int64_t n_slices, int64_t n_tokens, int64_t cap_tokens,
+                  void* out_fp16, int64_t out_slice_stride, void* hip_stream);
+
+/* Streaming state of the decode phase (CacheForge README, "How it works"
+ * and its figure on the quantization flow during prefill and decoding: the
+ * recent tokens stay fp16 while older ones are quantized).  Device arrays:
+ *   k_codes, k_scale, k_zero, v_codes, v_scale, v_zero
+ *       the key/value layouts above for cap_tokens tokens per slice;
+ *   k_ring, v_ring
+ *       fp16 [n_slices][R + G][D]: the fp16 residual of each slice as a
+ *       ring; residual token i (0 = oldest) sits in slot
+ *       (ring_head + i) mod (R + G).
+ * Host counters (owned by the caller, updated by the library):
+ *   n_slices    slices in every array.
+ *   cap_tokens  quantized-token capacity, a multiple of G.
+ *   n_quant     tokens quantized so far, a multiple of G, <= cap_tokens.
+ *   ring_head   slot of the oldest residual token, in [0, R + G).
+ *   ring_count  residual tokens, in [0, R + G - 1] between calls. */
+typedef struct kivi_stream {
+    int32_t* k_codes;
+    int32_t* v_codes;
+    void* k_scale;
+    void* k_zero;
+    void* v_scale;
+    void* v_zero;
+    void* k_ring;
+    void* v_ring;
+    int64_t n_slices;
+    int64_t cap_tokens;
+    int64_t n_quant;
+    int64_t ring_head;
+    int64_t ring_count;
+} kivi_stream;
+
+/* Prefill: quantizes the first floor((n_tokens - R)/G)*G tokens of every
+ * slice of k_fp16/v_fp16 (layout as for kivi_encode_k) into the stream's
+ * arrays and copies the remaining tokens into the rings in age order; sets
+ * n_quant to that token count, ring_head = 0 and ring_count to the rest.
+ * The stream's array pointers, n_slices and cap_tokens must be set; its
+ * counters are overwritten.  The rest is at most R + G - 1 tokens, so it
+ * always fits the ring.  KIVI_E_CAPACITY when the quantized prefix exceeds
+ * cap_tokens; KIVI_E_STATE when cap_tokens is not a multiple of G. */
+int kivi_stream_prefill(const kivi_config* cfg, kivi_stream* st,
+                        const void* k_fp16, const void* v_fp16,
+                        int64_t n_tokens, int64_t in_slice_stride, void* hip_stream);
+
+/* One decode step: appends k_new/v_new (fp16
+ * [n_slices][D], contiguous) to the residual; if the residual then holds
+ * more than R tokens and at least G, its oldest G tokens are quantized as
+ * key group n_quant/G and value rows n_quant .. n_quant+G-1 of every slice,
+ * and the counters advance (n_quant += G, ring_head += G mod R+G,
+ * ring_count -= G).  One kernel launch either way.  KIVI_E_CAPACITY (and
+ * nothing enqueued, counters unchanged) when that flush would pass
+ * cap_tokens. */
+int kivi_append_flush(const kivi_config* cfg, kivi_stream* st,
+                      const void* k_new_fp16, const void* v_new_fp16, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIVI_H */

@@ -4,3 +4,22 @@ The codec runs in hand-written HIP kernels behind the C ABI of ``libkivi``
 (declared in ``include/kivi.h``); this package is the thin Python binding
 over it.
 """
+
+from .binding import (  # noqa: E402,F401
+    Config,
+    KiviError,
+    Stream,
+    alloc_keys,
+    alloc_values,
+    kivi_append_flush,
+    kivi_decode_k,
+    kivi_decode_v,
+    kivi_encode_k,
+    kivi_encode_v,
+    kivi_k_code_words,
+    kivi_k_stat_elems,
+    kivi_ring_elems,
+    kivi_stream_prefill,
+    kivi_v_code_words,
+    kivi_v_stat_elems,
+)

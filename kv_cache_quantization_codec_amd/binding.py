@@ -1,0 +1,278 @@
+"""Thin Python binding over libkivi's C ABI (``include/kivi.h``).
+
+Argument marshalling only: every function takes torch tensors that live on
+the GPU, checks that their dtype and strides match the C layouts, and passes
+``data_ptr()`` values plus torch's current HIP stream to the entry point of
+the same name.  All codec work runs in the library's HIP kernels; there is no
+fallback of any kind -- importing this module fails loudly when
+``libkivi.so`` has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkivi.so")
+
+KIVI_OK = 0
+STATUS_NAMES = {
+    0: "KIVI_OK", -1: "KIVI_E_NULL", -2: "KIVI_E_BITS", -3: "KIVI_E_GROUP",
+    -4: "KIVI_E_HEAD_DIM", -5: "KIVI_E_RESIDUAL", -6: "KIVI_E_SHAPE", -7: "KIVI_E_ALIGN",
+    -8: "KIVI_E_CAPACITY", -9: "KIVI_E_STATE", -10: "KIVI_E_HIP",
+}
+
+
+class KiviError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().kivi_status_string(status).decode()} ({status})")
+
+
+class kivi_config(ctypes.Structure):
+    _fields_ = [("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("residual_length", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32)]
+
+
+class kivi_stream(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+                ("k_ring", ctypes.c_void_p), ("v_ring", ctypes.c_void_p),
+                ("n_slices", ctypes.c_int64), ("cap_tokens", ctypes.c_int64),
+                ("n_quant", ctypes.c_int64), ("ring_head", ctypes.c_int64),
+                ("ring_count", ctypes.c_int64)]
+
+
+# (name, restype, argtypes) of every symbol include/kivi.h declares
+_P, _I64, _I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_CFG = ctypes.POINTER(kivi_config)
+_ST = ctypes.POINTER(kivi_stream)
+SIGNATURES = [
+    ("kivi_status_string", ctypes.c_char_p, [_I32]),
+    ("kivi_last_hip_error", _I32, []),
+    ("kivi_validate_config", _I32, [_CFG]),
+    ("kivi_k_code_words", _I64, [_CFG, _I64]),
+    ("kivi_k_stat_elems", _I64, [_CFG, _I64]),
+    ("kivi_v_code_words", _I64, [_CFG, _I64]),
+    ("kivi_v_stat_elems", _I64, [_CFG, _I64]),
+    ("kivi_ring_elems", _I64, [_CFG]),
+    ("kivi_encode_k", _I32, [_CFG, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
+    ("kivi_encode_v", _I32, [_CFG, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
+    ("kivi_decode_k", _I32, [_CFG, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
+    ("kivi_decode_v", _I32, [_CFG, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
+    ("kivi_stream_prefill", _I32, [_CFG, _ST, _P, _P, _I64, _I64, _P]),
+    ("kivi_append_flush", _I32, [_CFG, _ST, _P, _P, _P]),
+]
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m kv_cache_quantization_codec_amd.build` (there is no fallback path)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+@dataclass(frozen=True)
+class Config:
+    k_bits: int = 2
+    v_bits: int = 2
+    group_size: int = 32
+    residual_length: int = 128
+    head_dim: int = 128
+
+    def c(self) -> kivi_config:
+        return kivi_config(self.k_bits, self.v_bits, self.group_size,
+                           self.residual_length, self.head_dim)
+
+
+def _cfg(cfg) -> ctypes.POINTER(kivi_config):
+    c = cfg.c() if isinstance(cfg, Config) else cfg
+    return ctypes.byref(c)
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _check(status: int, what: str):
+    if status != KIVI_OK:
+        raise KiviError(status, what)
+
+
+def _fp16_cache(t: torch.Tensor, D: int, what: str):
+    """(n_slices, slice_stride) of a [S, T, D] fp16 tensor with token stride D."""
+    if t.dtype != torch.float16 or t.dim() != 3 or t.shape[2] != D:
+        raise ValueError(f"{what}: expected float16 [S, T, {D}], got {t.dtype} {tuple(t.shape)}")
+    if t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != D):
+        raise ValueError(f"{what}: tokens must be contiguous rows of {D} elements")
+    return t.shape[0], t.stride(0)
+
+
+# ---------------------------------------------------------------------------
+# sizes
+# ---------------------------------------------------------------------------
+
+def kivi_k_code_words(cfg, n_tokens: int) -> int:
+    return lib().kivi_k_code_words(_cfg(cfg), n_tokens)
+
+
+def kivi_k_stat_elems(cfg, n_tokens: int) -> int:
+    return lib().kivi_k_stat_elems(_cfg(cfg), n_tokens)
+
+
+def kivi_v_code_words(cfg, n_tokens: int) -> int:
+    return lib().kivi_v_code_words(_cfg(cfg), n_tokens)
+
+
+def kivi_v_stat_elems(cfg, n_tokens: int) -> int:
+    return lib().kivi_v_stat_elems(_cfg(cfg), n_tokens)
+
+
+def kivi_ring_elems(cfg) -> int:
+    return lib().kivi_ring_elems(_cfg(cfg))
+
+
+def alloc_keys(cfg: Config, n_slices: int, cap_tokens: int, device="cuda"):
+    """Empty key payload (codes, scale, zero) for ``cap_tokens`` tokens per slice,
+    shaped like the C layouts."""
+    G, D = cfg.group_size, cfg.head_dim
+    ng = -(-cap_tokens // G)
+    W = G * cfg.k_bits // 32
+    codes = torch.empty((n_slices, ng * W, D), dtype=torch.int32, device=device)
+    scale = torch.empty((n_slices, ng, D), dtype=torch.float16, device=device)
+    zero = torch.empty((n_slices, ng, D), dtype=torch.float16, device=device)
+    return codes, scale, zero
+
+
+def alloc_values(cfg: Config, n_slices: int, cap_tokens: int, device="cuda"):
+    G, D = cfg.group_size, cfg.head_dim
+    ngv = -(-D // G)
+    W = G * cfg.v_bits // 32
+    codes = torch.empty((n_slices, cap_tokens, ngv * W), dtype=torch.int32, device=device)
+    scale = torch.empty((n_slices, cap_tokens, ngv), dtype=torch.float16, device=device)
+    zero = torch.empty((n_slices, cap_tokens, ngv), dtype=torch.float16, device=device)
+    return codes, scale, zero
+
+
+# ---------------------------------------------------------------------------
+# codec entry points
+# ---------------------------------------------------------------------------
+
+def kivi_encode_k(cfg, k: torch.Tensor, n_tokens: int, codes, scale, zero,
+                  cap_tokens: int | None = None, stream=None):
+    """Per-channel key quantization of tokens [0, n_tokens) of ``k`` [S, T, D]."""
+    S, stride = _fp16_cache(k, cfg.head_dim, "k")
+    cap = n_tokens if cap_tokens is None else cap_tokens
+    _check(lib().kivi_encode_k(_cfg(cfg), _ptr(k), S, n_tokens, stride, cap, _ptr(codes),
+                               _ptr(scale), _ptr(zero), _stream_ptr(stream)), "kivi_encode_k")
+
+
+def kivi_encode_v(cfg, v: torch.Tensor, n_tokens: int, codes, scale, zero,
+                  cap_tokens: int | None = None, stream=None):
+    """Per-token value quantization of rows [0, n_tokens) of ``v`` [S, T, D]."""
+    S, stride = _fp16_cache(v, cfg.head_dim, "v")
+    cap = n_tokens if cap_tokens is None else cap_tokens
+    _check(lib().kivi_encode_v(_cfg(cfg), _ptr(v), S, n_tokens, stride, cap, _ptr(codes),
+                               _ptr(scale), _ptr(zero), _stream_ptr(stream)), "kivi_encode_v")
+
+
+def kivi_decode_k(cfg, codes, scale, zero, n_tokens: int, out: torch.Tensor,
+                  cap_tokens: int | None = None, stream=None):
+    """Dequantize key tokens [0, n_tokens) into ``out`` [S, >=n_tokens, D]."""
+    S, stride = _fp16_cache(out, cfg.head_dim, "out")
+    cap = n_tokens if cap_tokens is None else cap_tokens
+    _check(lib().kivi_decode_k(_cfg(cfg), _ptr(codes), _ptr(scale), _ptr(zero), S, n_tokens, cap,
+                               _ptr(out), stride, _stream_ptr(stream)), "kivi_decode_k")
+
+
+def kivi_decode_v(cfg, codes, scale, zero, n_tokens: int, out: torch.Tensor,
+                  cap_tokens: int | None = None, stream=None):
+    S, stride = _fp16_cache(out, cfg.head_dim, "out")
+    cap = n_tokens if cap_tokens is None else cap_tokens
+    _check(lib().kivi_decode_v(_cfg(cfg), _ptr(codes), _ptr(scale), _ptr(zero), S, n_tokens, cap,
+                               _ptr(out), stride, _stream_ptr(stream)), "kivi_decode_v")
+
+
+# ---------------------------------------------------------------------------
+# streaming
+# ---------------------------------------------------------------------------
+
+class Stream:
+    """Device buffers and host counters of one streaming cache (``kivi_stream``)."""
+
+    def __init__(self, cfg: Config, n_slices: int, cap_tokens: int, device="cuda"):
+        G, R, D = cfg.group_size, cfg.residual_length, cfg.head_dim
+        if cap_tokens % G:
+            raise ValueError("cap_tokens must be a multiple of group_size")
+        self.cfg = cfg
+        self.keys = alloc_keys(cfg, n_slices, cap_tokens, device)
+        self.values = alloc_values(cfg, n_slices, cap_tokens, device)
+        self.k_ring = torch.empty((n_slices, R + G, D), dtype=torch.float16, device=device)
+        self.v_ring = torch.empty((n_slices, R + G, D), dtype=torch.float16, device=device)
+        kc, ks, kz = self.keys
+        vc, vs, vz = self.values
+        self.state = kivi_stream(_ptr(kc), _ptr(vc), _ptr(ks), _ptr(kz), _ptr(vs), _ptr(vz),
+                                 _ptr(self.k_ring), _ptr(self.v_ring), n_slices, cap_tokens,
+                                 0, 0, 0)
+
+    @property
+    def n_quant(self) -> int:
+        return self.state.n_quant
+
+    @property
+    def ring_head(self) -> int:
+        return self.state.ring_head
+
+    @property
+    def ring_count(self) -> int:
+        return self.state.ring_count
+
+    def residual(self):
+        """Residual K and V tokens in age order, fp16 [S, count, D] (copies)."""
+        slots = self.k_ring.shape[1]
+        idx = [(self.ring_head + i) % slots for i in range(self.ring_count)]
+        return self.k_ring[:, idx], self.v_ring[:, idx]
+
+
+def kivi_stream_prefill(st: Stream, k: torch.Tensor, v: torch.Tensor, n_tokens: int, stream=None):
+    S, stride = _fp16_cache(k, st.cfg.head_dim, "k")
+    S2, stride2 = _fp16_cache(v, st.cfg.head_dim, "v")
+    if S != st.state.n_slices or S2 != S or stride2 != stride:
+        raise ValueError("k and v must match the stream's slices and share one stride")
+    _check(lib().kivi_stream_prefill(_cfg(st.cfg), ctypes.byref(st.state), _ptr(k), _ptr(v),
+                                     n_tokens, stride, _stream_ptr(stream)), "kivi_stream_prefill")
+
+
+def kivi_append_flush(st: Stream, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> bool:
+    """One decode step; returns True when a group was flushed."""
+    D = st.cfg.head_dim
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        if t.dtype != torch.float16 or tuple(t.shape) != (st.state.n_slices, D) or not t.is_contiguous():
+            raise ValueError(f"{nm}: expected contiguous float16 [{st.state.n_slices}, {D}]")
+    before = st.state.n_quant
+    _check(lib().kivi_append_flush(_cfg(st.cfg), ctypes.byref(st.state), _ptr(k_new), _ptr(v_new),
+                                   _stream_ptr(stream)), "kivi_append_flush")
+    return st.state.n_quant != before

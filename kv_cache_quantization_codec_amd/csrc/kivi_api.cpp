@@ -1,0 +1,323 @@
+// Host-side entry points of libkivi: argument validation, sizing and the
+// streaming counters.  Plain C++ with no HIP header, so every check here runs
+// (and is tested) without a GPU; work is handed to the launchers declared in
+// kivi_launch.h only after all checks passed.
+//
+// Sizes follow the layouts of include/kivi.h (CacheSeek PR #4 "Feature
+// (quantization): add KIVI KV-cache quantization for exact-prefix reuse":
+// int32-packed codes plus scale/offset sidecars, sized by the manager).
+
+#include "../../include/kivi.h"
+#include "kivi_launch.h"
+
+#include <stdint.h>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxTokens = (int64_t(1) << 30);   // per slice, fits int32 math in kernels
+
+bool valid_bits(int32_t b) { return b == 2 || b == 4 || b == 8; }
+bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+int check_config(const kivi_config* c) {
+    if (!c) return KIVI_E_NULL;
+    if (!valid_bits(c->k_bits) || !valid_bits(c->v_bits)) return KIVI_E_BITS;
+    if (!valid_group(c->group_size)) return KIVI_E_GROUP;
+    if (c->head_dim < 8 || c->head_dim > 256 || c->head_dim % 8 != 0) return KIVI_E_HEAD_DIM;
+    if (c->residual_length < 0) return KIVI_E_RESIDUAL;
+    return KIVI_OK;
+}
+
+// per-slice sizes; n >= 0 and a valid config assumed
+int64_t k_words(const kivi_config* c, int64_t n) {
+    return ceil_div(n, c->group_size) * (c->group_size * c->k_bits / 32) * c->head_dim;
+}
+int64_t k_stats(const kivi_config* c, int64_t n) { return ceil_div(n, c->group_size) * c->head_dim; }
+int64_t v_groups(const kivi_config* c) { return ceil_div(c->head_dim, c->group_size); }
+int64_t v_words(const kivi_config* c, int64_t n) {
+    return n * v_groups(c) * (c->group_size * c->v_bits / 32);
+}
+int64_t v_stats(const kivi_config* c, int64_t n) { return n * v_groups(c); }
+
+int record(int hip_err) {
+    if (hip_err != 0) {
+        g_last_hip_error = hip_err;
+        return KIVI_E_HIP;
+    }
+    return KIVI_OK;
+}
+
+// Checks shared by encode and decode: counts, strides and the total size of
+// every array addressed (so that no index overflows int64).
+int check_common(const kivi_config* c, int64_t n_slices, int64_t n_tokens, int64_t cap_tokens,
+                 int64_t fp16_stride, bool keys) {
+    if (n_slices < 0 || n_tokens < 0 || cap_tokens < n_tokens) return KIVI_E_SHAPE;
+    if (n_tokens > kMaxTokens || cap_tokens > kMaxTokens) return KIVI_E_SHAPE;
+    if (fp16_stride % 8 != 0) return KIVI_E_ALIGN;
+    int64_t need = 0;
+    if (!mul_ok(n_tokens, c->head_dim, &need) || fp16_stride < need) return KIVI_E_SHAPE;
+    int64_t total = 0;
+    if (!mul_ok(n_slices, fp16_stride, &total)) return KIVI_E_SHAPE;
+    const int64_t words = keys ? k_words(c, cap_tokens) : v_words(c, cap_tokens);
+    if (!mul_ok(n_slices, words, &total) || !mul_ok(total, 4, &total)) return KIVI_E_SHAPE;
+    return KIVI_OK;
+}
+
+int encode(bool keys, const kivi_config* cfg, const void* in, int64_t n_slices, int64_t n_tokens,
+           int64_t in_stride, int64_t cap_tokens, int32_t* codes, void* scale, void* zero,
+           void* stream) {
+    int st = check_config(cfg);
+    if (st) return st;
+    if (n_slices == 0 || n_tokens == 0) {
+        if (n_slices < 0 || n_tokens < 0) return KIVI_E_SHAPE;
+        return KIVI_OK;
+    }
+    st = check_common(cfg, n_slices, n_tokens, cap_tokens, in_stride, keys);
+    if (st) return st;
+    if (!in || !codes || !scale || !zero) return KIVI_E_NULL;
+    if (!aligned16(in) || !aligned16(codes) || !aligned16(scale) || !aligned16(zero)) return KIVI_E_ALIGN;
+    kivi::EncodeArgs a;
+    a.in = static_cast<const uint16_t*>(in);
+    a.in_stride = in_stride;
+    a.n_slices = n_slices;
+    a.n_tokens = static_cast<int32_t>(n_tokens);
+    a.cap_tokens = static_cast<int32_t>(cap_tokens);
+    a.head_dim = cfg->head_dim;
+    a.group_size = cfg->group_size;
+    a.bits = keys ? cfg->k_bits : cfg->v_bits;
+    a.codes = reinterpret_cast<uint32_t*>(codes);
+    a.scale = static_cast<uint16_t*>(scale);
+    a.zero = static_cast<uint16_t*>(zero);
+    return record(keys ? kivi::launch_encode_k(a, stream) : kivi::launch_encode_v(a, stream));
+}
+
+int decode(bool keys, const kivi_config* cfg, const int32_t* codes, const void* scale, const void* zero,
+           int64_t n_slices, int64_t n_tokens, int64_t cap_tokens, void* out, int64_t out_stride,
+           void* stream) {
+    int st = check_config(cfg);
+    if (st) return st;
+    if (n_slices == 0 || n_tokens == 0) {
+        if (n_slices < 0 || n_tokens < 0) return KIVI_E_SHAPE;
+        return KIVI_OK;
+    }
+    st = check_common(cfg, n_slices, n_tokens, cap_tokens, out_stride, keys);
+    if (st) return st;
+    if (!codes || !scale || !zero || !out) return KIVI_E_NULL;
+    if (!aligned16(codes) || !aligned16(scale) || !aligned16(zero) || !aligned16(out)) return KIVI_E_ALIGN;
+    kivi::DecodeArgs a;
+    a.codes = reinterpret_cast<const uint32_t*>(codes);
+    a.scale = static_cast<const uint16_t*>(scale);
+    a.zero = static_cast<const uint16_t*>(zero);
+    a.n_slices = n_slices;
+    a.n_tokens = static_cast<int32_t>(n_tokens);
+    a.cap_tokens = static_cast<int32_t>(cap_tokens);
+    a.head_dim = cfg->head_dim;
+    a.group_size = cfg->group_size;
+    a.bits = keys ? cfg->k_bits : cfg->v_bits;
+    a.out = static_cast<uint16_t*>(out);
+    a.out_stride = out_stride;
+    return record(keys ? kivi::launch_decode_k(a, stream) : kivi::launch_decode_v(a, stream));
+}
+
+// Pointers, capacity and counters of a stream (counters are checked only when
+// `counters` is set: the prefill overwrites them).
+int check_stream(const kivi_config* c, const kivi_stream* s, bool counters) {
+    if (!s) return KIVI_E_NULL;
+    if (s->n_slices < 0) return KIVI_E_SHAPE;
+    const int64_t G = c->group_size;
+    const int64_t slots = int64_t(c->residual_length) + G;
+    if (s->cap_tokens < 0 || s->cap_tokens > kMaxTokens || s->cap_tokens % G != 0) return KIVI_E_STATE;
+    if (slots > kMaxTokens) return KIVI_E_SHAPE;
+    if (counters) {
+        if (s->n_quant < 0 || s->n_quant % G != 0 || s->n_quant > s->cap_tokens) return KIVI_E_STATE;
+        if (s->ring_head < 0 || s->ring_head >= slots) return KIVI_E_STATE;
+        if (s->ring_count < 0 || s->ring_count > slots - 1) return KIVI_E_STATE;
+    }
+    if (s->n_slices == 0) return KIVI_OK;
+    int64_t total = 0;
+    if (!mul_ok(s->n_slices, slots * c->head_dim, &total)) return KIVI_E_SHAPE;
+    if (!mul_ok(s->n_slices, k_words(c, s->cap_tokens) + v_words(c, s->cap_tokens), &total) ||
+        !mul_ok(total, 4, &total))
+        return KIVI_E_SHAPE;
+    if (!s->k_codes || !s->v_codes || !s->k_scale || !s->k_zero || !s->v_scale || !s->v_zero ||
+        !s->k_ring || !s->v_ring)
+        return KIVI_E_NULL;
+    if (!aligned16(s->k_codes) || !aligned16(s->v_codes) || !aligned16(s->k_scale) ||
+        !aligned16(s->k_zero) || !aligned16(s->v_scale) || !aligned16(s->v_zero) ||
+        !aligned16(s->k_ring) || !aligned16(s->v_ring))
+        return KIVI_E_ALIGN;
+    return KIVI_OK;
+}
+
+bool flush_due(int64_t count, int64_t residual, int64_t group) {
+    return count > residual && count >= group;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kivi_status_string(int status) {
+    switch (status) {
+        case KIVI_OK: return "KIVI_OK";
+        case KIVI_E_NULL: return "KIVI_E_NULL: a required pointer is NULL";
+        case KIVI_E_BITS: return "KIVI_E_BITS: k_bits and v_bits must be 2, 4 or 8";
+        case KIVI_E_GROUP: return "KIVI_E_GROUP: group_size must be 32, 64 or 128";
+        case KIVI_E_HEAD_DIM: return "KIVI_E_HEAD_DIM: head_dim must be a multiple of 8 in [8, 256]";
+        case KIVI_E_RESIDUAL: return "KIVI_E_RESIDUAL: residual_length must be >= 0";
+        case KIVI_E_SHAPE: return "KIVI_E_SHAPE: bad count, stride or capacity";
+        case KIVI_E_ALIGN: return "KIVI_E_ALIGN: pointers must be 16-byte aligned, strides multiples of 8";
+        case KIVI_E_CAPACITY: return "KIVI_E_CAPACITY: the quantized store is full";
+        case KIVI_E_STATE: return "KIVI_E_STATE: inconsistent stream counters";
+        case KIVI_E_HIP: return "KIVI_E_HIP: a HIP launch failed";
+        default: return "unknown kivi status";
+    }
+}
+
+int kivi_last_hip_error(void) { return g_last_hip_error; }
+
+int kivi_validate_config(const kivi_config* cfg) { return check_config(cfg); }
+
+int64_t kivi_k_code_words(const kivi_config* cfg, int64_t n) {
+    return (check_config(cfg) || n < 0) ? -1 : k_words(cfg, n);
+}
+int64_t kivi_k_stat_elems(const kivi_config* cfg, int64_t n) {
+    return (check_config(cfg) || n < 0) ? -1 : k_stats(cfg, n);
+}
+int64_t kivi_v_code_words(const kivi_config* cfg, int64_t n) {
+    return (check_config(cfg) || n < 0) ? -1 : v_words(cfg, n);
+}
+int64_t kivi_v_stat_elems(const kivi_config* cfg, int64_t n) {
+    return (check_config(cfg) || n < 0) ? -1 : v_stats(cfg, n);
+}
+int64_t kivi_ring_elems(const kivi_config* cfg) {
+    return check_config(cfg) ? -1 : (int64_t(cfg->residual_length) + cfg->group_size) * cfg->head_dim;
+}
+
+int kivi_encode_k(const kivi_config* cfg, const void* k, int64_t n_slices, int64_t n_tokens,
+                  int64_t in_stride, int64_t cap, int32_t* codes, void* scale, void* zero,
+                  void* stream) {
+    return encode(true, cfg, k, n_slices, n_tokens, in_stride, cap, codes, scale, zero, stream);
+}
+
+int kivi_encode_v(const kivi_config* cfg, const void* v, int64_t n_slices, int64_t n_tokens,
+                  int64_t in_stride, int64_t cap, int32_t* codes, void* scale, void* zero,
+                  void* stream) {
+    return encode(false, cfg, v, n_slices, n_tokens, in_stride, cap, codes, scale, zero, stream);
+}
+
+int kivi_decode_k(const kivi_config* cfg, const int32_t* codes, const void* scale, const void* zero,
+                  int64_t n_slices, int64_t n_tokens, int64_t cap, void* out, int64_t out_stride,
+                  void* stream) {
+    return decode(true, cfg, codes, scale, zero, n_slices, n_tokens, cap, out, out_stride, stream);
+}
+
+int kivi_decode_v(const kivi_config* cfg, const int32_t* codes, const void* scale, const void* zero,
+                  int64_t n_slices, int64_t n_tokens, int64_t cap, void* out, int64_t out_stride,
+                  void* stream) {
+    return decode(false, cfg, codes, scale, zero, n_slices, n_tokens, cap, out, out_stride, stream);
+}
+
+int kivi_stream_prefill(const kivi_config* cfg, kivi_stream* st, const void* k, const void* v,
+                        int64_t n_tokens, int64_t in_stride, void* stream) {
+    int s = check_config(cfg);
+    if (s) return s;
+    s = check_stream(cfg, st, false);
+    if (s) return s;
+    if (n_tokens < 0 || n_tokens > kMaxTokens) return KIVI_E_SHAPE;
+    const int64_t G = cfg->group_size, R = cfg->residual_length;
+    const int64_t nq = (n_tokens > R ? (n_tokens - R) / G : 0) * G;
+    const int64_t rest = n_tokens - nq;           // <= R + G - 1 by construction
+    if (nq > st->cap_tokens) return KIVI_E_CAPACITY;
+    if (st->n_slices > 0 && n_tokens > 0) {
+        if (in_stride % 8 != 0) return KIVI_E_ALIGN;
+        int64_t need = 0, total = 0;
+        if (!mul_ok(n_tokens, cfg->head_dim, &need) || in_stride < need) return KIVI_E_SHAPE;
+        if (!mul_ok(st->n_slices, in_stride, &total)) return KIVI_E_SHAPE;
+        if (!k || !v) return KIVI_E_NULL;
+        if (!aligned16(k) || !aligned16(v)) return KIVI_E_ALIGN;
+        if (nq > 0) {
+            s = kivi_encode_k(cfg, k, st->n_slices, nq, in_stride, st->cap_tokens, st->k_codes,
+                              st->k_scale, st->k_zero, stream);
+            if (s) return s;
+            s = kivi_encode_v(cfg, v, st->n_slices, nq, in_stride, st->cap_tokens, st->v_codes,
+                              st->v_scale, st->v_zero, stream);
+            if (s) return s;
+        }
+        if (rest > 0) {
+            kivi::RingFillArgs a;
+            a.k_in = static_cast<const uint16_t*>(k);
+            a.v_in = static_cast<const uint16_t*>(v);
+            a.in_stride = in_stride;
+            a.n_slices = st->n_slices;
+            a.first_token = static_cast<int32_t>(nq);
+            a.n_tokens = static_cast<int32_t>(rest);
+            a.head_dim = cfg->head_dim;
+            a.ring_slots = static_cast<int32_t>(R + G);
+            a.k_ring = static_cast<uint16_t*>(st->k_ring);
+            a.v_ring = static_cast<uint16_t*>(st->v_ring);
+            s = record(kivi::launch_ring_fill(a, stream));
+            if (s) return s;
+        }
+    }
+    st->n_quant = nq;
+    st->ring_head = 0;
+    st->ring_count = rest;
+    return KIVI_OK;
+}
+
+int kivi_append_flush(const kivi_config* cfg, kivi_stream* st, const void* k_new, const void* v_new,
+                      void* stream) {
+    int s = check_config(cfg);
+    if (s) return s;
+    s = check_stream(cfg, st, true);
+    if (s) return s;
+    const int64_t G = cfg->group_size, R = cfg->residual_length;
+    const int64_t slots = R + G;
+    const bool flush = flush_due(st->ring_count + 1, R, G);
+    if (flush && st->n_quant + G > st->cap_tokens) return KIVI_E_CAPACITY;
+    if (st->n_slices > 0) {
+        if (!k_new || !v_new) return KIVI_E_NULL;
+        if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_E_ALIGN;
+        kivi::StepArgs a;
+        a.k_new = static_cast<const uint16_t*>(k_new);
+        a.v_new = static_cast<const uint16_t*>(v_new);
+        a.k_ring = static_cast<uint16_t*>(st->k_ring);
+        a.v_ring = static_cast<uint16_t*>(st->v_ring);
+        a.k_codes = reinterpret_cast<uint32_t*>(st->k_codes);
+        a.k_scale = static_cast<uint16_t*>(st->k_scale);
+        a.k_zero = static_cast<uint16_t*>(st->k_zero);
+        a.v_codes = reinterpret_cast<uint32_t*>(st->v_codes);
+        a.v_scale = static_cast<uint16_t*>(st->v_scale);
+        a.v_zero = static_cast<uint16_t*>(st->v_zero);
+        a.n_slices = st->n_slices;
+        a.cap_tokens = static_cast<int32_t>(st->cap_tokens);
+        a.head_dim = cfg->head_dim;
+        a.group_size = cfg->group_size;
+        a.k_bits = cfg->k_bits;
+        a.v_bits = cfg->v_bits;
+        a.ring_slots = static_cast<int32_t>(slots);
+        a.ring_head = static_cast<int32_t>(st->ring_head);
+        a.ring_count = static_cast<int32_t>(st->ring_count);
+        a.flush = flush ? 1 : 0;
+        a.n_quant = static_cast<int32_t>(st->n_quant);
+        s = record(kivi::launch_append_flush(a, stream));
+        if (s) return s;
+    }
+    st->ring_count += 1;
+    if (flush) {
+        st->n_quant += G;
+        st->ring_head = (st->ring_head + G) % slots;
+        st->ring_count -= G;
+    }
+    return KIVI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,736 @@
+// HIP kernels of libkivi for gfx950 (MI355X), and their launchers.
+//
+// The codec (CacheForge README, "How it works"; CacheSeek PR #4 "Feature
+// (quantization): add KIVI KV-cache quantization for exact-prefix reuse"):
+// keys are quantized per channel over groups of G tokens, values per token
+// over groups of G channels, each group with an fp16 scale and zero taken
+// from its min and max, codes of b bits packed LSB-first into 32-bit words,
+// partial groups padded with code 0.  Arithmetic (the reading the pages
+// leave open, stated once): scale = fp16(fp32(fp32(mx - mn) / (2^b - 1))),
+// zero = mn, q = clamp(rint(fp32(fp32(x - zero) / scale)), 0, 2^b - 1) with
+// round-half-even and IEEE division, q = 0 when scale == 0, and
+// xhat = fp16(fp32(q * scale + zero)).
+//
+// Everything here is HBM-bandwidth bound (about 2.4-3.1 bytes moved per
+// element each way), so there is no MFMA: the design goals are full-width
+// (16-byte) coalesced global accesses, cheap cross-lane reductions, and as
+// few VALU instructions per element as the exact arithmetic allows.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kivi_launch.h"
+
+namespace kivi {
+namespace {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte access
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 256;
+constexpr int kMaxGrid = 1 << 22;
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ uint32_t as_u32(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ float lo_f32(uint32_t u) {
+    return (float)__builtin_bit_cast(f16, (uint16_t)(u & 0xFFFFu));
+}
+__device__ __forceinline__ float hi_f32(uint32_t u) {
+    return (float)__builtin_bit_cast(f16, (uint16_t)(u >> 16));
+}
+__device__ __forceinline__ f16x2 pmin(f16x2 a, f16x2 b) { return __builtin_elementwise_min(a, b); }
+__device__ __forceinline__ f16x2 pmax(f16x2 a, f16x2 b) { return __builtin_elementwise_max(a, b); }
+
+// Exchange within the wave (all lanes active).  CTRL is a DPP control word:
+// 0xB1 = quad_perm[1,0,3,2] (lane ^ 1), 0x4E = quad_perm[2,3,0,1] (lane ^ 2),
+// 0x141 = row_half_mirror (within 8 lanes), 0x140 = row_mirror (within 16).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Per-group quantization parameters.
+struct QParams {
+    float zero;     // the group minimum, +0 for a zero of either sign
+    float scale;    // fp16 scale widened to fp32
+    float rcp;      // ~1/scale (within 1 ulp), 0 when scale == 0
+};
+
+// Statistics -> parameters.  mn/mx are fp16 values held in fp32 (exact).
+//   scale = fp16(fp32(fp32(mx - mn) / (2^b - 1)))
+// The fp32 quotient is computed as fp32(fp64(rng) * fp64(1/(2^b-1))): for any
+// fp32 rng the fp64 product is within 2^-52 (relative) of rng/(2^b-1), while
+// rng/(2^b-1) for an odd divisor below 2^8 is never within 2^-41 of an fp32
+// rounding midpoint, so the final rounding equals that of the exact quotient.
+// The empty asm keeps the fp32 step: without it the compiler merges the two
+// narrowing conversions into one fp64->fp16 rounding, a different result.
+template <int BITS>
+__device__ __forceinline__ QParams make_params(float mn, float mx, uint32_t& scale_bits,
+                                               uint32_t& zero_bits) {
+    constexpr double kInvLevels = 1.0 / (double)((1 << BITS) - 1);
+    mn = mn + 0.0f;                       // -0 -> +0 (round-to-nearest)
+    mx = mx + 0.0f;
+    const float rng = mx - mn;
+    float s32 = (float)((double)rng * kInvLevels);
+    asm volatile("" : "+v"(s32));
+    const f16 sh = (f16)s32;
+    QParams p;
+    p.scale = (float)sh;
+    p.zero = mn;
+    p.rcp = (p.scale == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(p.scale);
+    scale_bits = __builtin_bit_cast(uint16_t, sh);
+    zero_bits = __builtin_bit_cast(uint16_t, (f16)mn);
+    return p;
+}
+
+// Code of one element.  Fast path: y = d * rcp, which differs from the exact
+// fp32 quotient Q = fp32(d / scale) by at most 2^-22 * Q (1-ulp reciprocal
+// plus two roundings), i.e. by at most 2^-14 for Q <= 256.  Unless y lies
+// within 2^-12 of a half-integer, rint(y) == rint(Q); inside that band the
+// IEEE division is done (correctly rounded: no fast-math).  Values above the
+// top level are clamped; y >= 2^b - 1 already implies clamp(rint(Q)) = 2^b-1.
+template <int BITS>
+__device__ __forceinline__ uint32_t quant1(float x, const QParams& p) {
+    constexpr float kTop = (float)((1 << BITS) - 1);
+    const float d = x - p.zero;
+    const float y = d * p.rcp;
+    const float yc = __builtin_fminf(y, kTop);
+    const float r = __builtin_rintf(yc);
+    uint32_t q = (uint32_t)r;
+    if (__builtin_fabsf(yc - r) > 0.5f - 0x1p-12f) {
+        q = (uint32_t)__builtin_fminf(__builtin_rintf(d / p.scale), kTop);
+    }
+    return q;
+}
+
+// fp16 of fp32(q * scale + zero); q * scale is exact in fp32, so the fma
+// rounds once to fp32.  The empty asm keeps that fp32 result from being
+// fused with the narrowing conversion into a single rounding to fp16.
+__device__ __forceinline__ f16 dequant1(uint32_t q, float scale, float zero) {
+    float y = __builtin_fmaf((float)q, scale, zero);
+    asm volatile("" : "+v"(y));
+    return (f16)y;
+}
+
+// ---------------------------------------------------------------------------
+// keys: one channel pair of one tile (G tokens x D channels) staged in LDS
+// ---------------------------------------------------------------------------
+
+// Quantizes channels 2p, 2p+1 of one key group from LDS column `col` (dword
+// stride `half_d`) with `nv` valid tokens, and stores its W code words per
+// channel and both sidecars.  `grp` is the group's index in the (slice,
+// group) output arrays.
+template <int BITS, int G, bool FULL>
+__device__ __forceinline__ void key_column(const uint32_t* col, int half_d, int nv, int D, int p,
+                                           int64_t grp, uint32_t* __restrict__ codes,
+                                           uint16_t* __restrict__ scale,
+                                           uint16_t* __restrict__ zero) {
+    constexpr int W = G * BITS / 32;
+    constexpr int PER = 32 / BITS;
+    uint32_t v[G];
+#pragma unroll
+    for (int t = 0; t < G; ++t) v[t] = col[(FULL ? t : (t < nv ? t : nv - 1)) * half_d];
+    f16x2 mn = as_h2(v[0]), mx = mn;
+#pragma unroll
+    for (int t = 1; t < G; ++t) {
+        mn = pmin(mn, as_h2(v[t]));
+        mx = pmax(mx, as_h2(v[t]));
+    }
+    uint32_t sb0, zb0, sb1, zb1;
+    const QParams p0 = make_params<BITS>((float)mn.x, (float)mx.x, sb0, zb0);
+    const QParams p1 = make_params<BITS>((float)mn.y, (float)mx.y, sb1, zb1);
+    uint32_t w0[W], w1[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        w0[w] = 0;
+        w1[w] = 0;
+    }
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+        uint32_t q0 = quant1<BITS>(lo_f32(v[t]), p0);
+        uint32_t q1 = quant1<BITS>(hi_f32(v[t]), p1);
+        if (!FULL && t >= nv) {
+            q0 = 0;
+            q1 = 0;
+        }
+        w0[t / PER] |= q0 << ((t % PER) * BITS);
+        w1[t / PER] |= q1 << ((t % PER) * BITS);
+    }
+    uint32_t* cdst = codes + grp * (int64_t)(W * D) + 2 * p;
+#pragma unroll
+    for (int w = 0; w < W; ++w) *reinterpret_cast<u32x2*>(cdst + w * D) = u32x2{w0[w], w1[w]};
+    *reinterpret_cast<uint32_t*>(scale + grp * D + 2 * p) = sb0 | (sb1 << 16);
+    *reinterpret_cast<uint32_t*>(zero + grp * D + 2 * p) = zb0 | (zb1 << 16);
+}
+
+// Full-cache key encode.  A block stages `tpb` consecutive groups of one slice
+// (tpb*G tokens x D channels, contiguous in HBM) into LDS with 16-byte loads;
+// thread (ti, p) then owns channel pair p of group ti for all G tokens.
+template <int BITS, int G>
+__global__ void __launch_bounds__(kBlock)
+encode_k_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int n_tokens, int D, int ng,
+                int tpb, int batches_per_slice, int64_t n_batches, uint32_t* __restrict__ codes,
+                uint16_t* __restrict__ scale, uint16_t* __restrict__ zero, int out_groups) {
+    extern __shared__ u32x4 lds4[];
+    const int half_d = D >> 1;
+    const int tid = threadIdx.x;
+    const int ti = tid / half_d;
+    const int p = tid - ti * half_d;
+    const uint32_t* lds = reinterpret_cast<const uint32_t*>(lds4);
+    for (int64_t batch = blockIdx.x; batch < n_batches; batch += gridDim.x) {
+        const int64_t s = batch / batches_per_slice;
+        const int g0 = (int)(batch - s * batches_per_slice) * tpb;
+        const int t0 = g0 * G;
+        const int nt = min(tpb * G, n_tokens - t0);
+        const u32x4* src = reinterpret_cast<const u32x4*>(in + s * in_stride + (int64_t)t0 * D);
+        const int nchunks = nt * (D >> 3);
+        __syncthreads();
+        for (int base = 0; base < nchunks; base += 8 * kBlock) {
+            u32x4 r[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = base + j * kBlock + tid;
+                if (c < nchunks) r[j] = __builtin_nontemporal_load(src + c);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = base + j * kBlock + tid;
+                if (c < nchunks) lds4[c] = r[j];
+            }
+        }
+        __syncthreads();
+        const int g = g0 + ti;
+        if (ti < tpb && g < ng) {
+            const int nv = min(G, n_tokens - g * G);
+            const uint32_t* col = lds + ti * G * half_d + p;
+            const int64_t grp = s * out_groups + g;
+            if (nv == G)
+                key_column<BITS, G, true>(col, half_d, nv, D, p, grp, codes, scale, zero);
+            else
+                key_column<BITS, G, false>(col, half_d, nv, D, p, grp, codes, scale, zero);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// values: one 8-channel chunk of one token row per lane
+// ---------------------------------------------------------------------------
+
+// Lane c of a token row (lanes-per-row a power of two >= G/8) holds channels
+// 8c .. 8c+7 in `x`; lanes c >= D/8 are padding (`cvalid` false).  All lanes
+// of the wave must call this together (DPP reductions inside).  Stores the
+// row's code words and, from the first lane of each group, its sidecars,
+// when `store` is set.
+template <int BITS, int G>
+__device__ __forceinline__ void value_chunk(const u32x4& x, bool cvalid, int c, bool store,
+                                            uint32_t* __restrict__ row_codes,
+                                            uint16_t* __restrict__ row_scale,
+                                            uint16_t* __restrict__ row_zero) {
+    constexpr int GL = G / 8;                 // lanes per value group
+    const f16x2 a0 = as_h2(x.x), a1 = as_h2(x.y), a2 = as_h2(x.z), a3 = as_h2(x.w);
+    const f16x2 mn2 = pmin(pmin(a0, a1), pmin(a2, a3));
+    const f16x2 mx2 = pmax(pmax(a0, a1), pmax(a2, a3));
+    f16 mn = mn2.x < mn2.y ? mn2.x : mn2.y;
+    f16 mx = mx2.x > mx2.y ? mx2.x : mx2.y;
+    if (!cvalid) {
+        mn = (f16)__builtin_inff();
+        mx = (f16)(-__builtin_inff());
+    }
+    // reduce (min, -max) over the group's lanes with one packed min per step
+    f16x2 pr;
+    pr.x = mn;
+    pr.y = -mx;
+    uint32_t pu = as_u32(pr);
+    if (GL >= 2) pu = as_u32(pmin(as_h2(pu), as_h2(dpp<0xB1>(pu))));
+    if (GL >= 4) pu = as_u32(pmin(as_h2(pu), as_h2(dpp<0x4E>(pu))));
+    if (GL >= 8) pu = as_u32(pmin(as_h2(pu), as_h2(dpp<0x141>(pu))));
+    if (GL >= 16) pu = as_u32(pmin(as_h2(pu), as_h2(dpp<0x140>(pu))));
+    pr = as_h2(pu);
+    uint32_t sb, zb;
+    const QParams prm = make_params<BITS>((float)pr.x, -(float)pr.y, sb, zb);
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+    uint32_t q[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        q[2 * i] = quant1<BITS>(lo_f32(xs[i]), prm);
+        q[2 * i + 1] = quant1<BITS>(hi_f32(xs[i]), prm);
+    }
+    if (!cvalid) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = 0;
+    }
+    if (BITS == 4) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w |= q[i] << (4 * i);
+        if (store) row_codes[c] = w;
+    } else if (BITS == 8) {
+        const uint32_t w0 = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        const uint32_t w1 = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+        if (store) *reinterpret_cast<u32x2*>(row_codes + 2 * c) = u32x2{w0, w1};
+    } else {
+        uint32_t h = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h |= q[i] << (2 * i);
+        const uint32_t nb = dpp<0xB1>(h);
+        if (store && (c & 1) == 0) row_codes[c >> 1] = h | (nb << 16);
+    }
+    if (store && (c % GL) == 0) {
+        row_scale[c / GL] = (uint16_t)sb;
+        row_zero[c / GL] = (uint16_t)zb;
+    }
+}
+
+// Full-cache value encode: a block covers `rows_per_block` token rows of one
+// slice; 2^lpt_log2 lanes per row.
+template <int BITS, int G>
+__global__ void __launch_bounds__(kBlock)
+encode_v_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int n_tokens, int D,
+                int lpt_log2, int rows_per_block, int blocks_per_slice, int64_t n_blocks,
+                uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
+                uint16_t* __restrict__ zero, int cap, int ngv) {
+    constexpr int GL = G / 8;
+    const int lpt = 1 << lpt_log2;
+    const int c = threadIdx.x & (lpt - 1);
+    const int r0 = threadIdx.x >> lpt_log2;
+    const int rstep = kBlock >> lpt_log2;
+    const bool cvalid = c < (D >> 3);
+    const bool in_group = (c / GL) < ngv;
+    const int wpt = ngv * G * BITS / 32;
+    for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+        const int64_t s = blk / blocks_per_slice;
+        const int tb = (int)(blk - s * blocks_per_slice) * rows_per_block;
+        const uint16_t* src = in + s * in_stride;
+        for (int r = r0; r < rows_per_block; r += rstep) {
+            const int t = tb + r;
+            const bool rvalid = t < n_tokens;
+            u32x4 x = u32x4{0, 0, 0, 0};
+            if (rvalid && cvalid)
+                x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)t * D + 8 * c));
+            const int64_t row = s * cap + t;
+            value_chunk<BITS, G>(x, cvalid, c, rvalid && in_group, codes + row * wpt,
+                                 scale + row * ngv, zero + row * ngv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void widen8(const u32x4& h, float* f) {
+    const uint32_t u[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = lo_f32(u[i]);
+        f[2 * i + 1] = hi_f32(u[i]);
+    }
+}
+
+__device__ __forceinline__ uint32_t pack2(f16 a, f16 b) {
+    f16x2 h;
+    h.x = a;
+    h.y = b;
+    return as_u32(h);
+}
+
+// Keys: lane c of a tile owns channels 8c..8c+7 of one group for all its
+// tokens; per token it writes 16 bytes of the token-major output.
+template <int BITS, int G>
+__global__ void __launch_bounds__(kBlock)
+decode_k_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
+                const uint16_t* __restrict__ zero, int n_tokens, int D, int ng, int out_groups,
+                int tiles_per_block, int64_t n_tiles, int64_t n_blocks, uint16_t* __restrict__ out,
+                int64_t out_stride) {
+    constexpr int W = G * BITS / 32;
+    constexpr int PER = 32 / BITS;
+    constexpr uint32_t kMask = (1u << BITS) - 1u;
+    const int cpr = D >> 3;
+    const int ti = threadIdx.x / cpr;
+    const int c = threadIdx.x - ti * cpr;
+    if (ti >= tiles_per_block) return;
+    for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+        const int64_t tile = blk * tiles_per_block + ti;
+        if (tile >= n_tiles) continue;
+        const int64_t s = tile / ng;
+        const int g = (int)(tile - s * ng);
+        const int nv = min(G, n_tokens - g * G);
+        const int64_t grp = s * out_groups + g;
+        float sf[8], zf[8];
+        widen8(*reinterpret_cast<const u32x4*>(scale + grp * D + 8 * c), sf);
+        widen8(*reinterpret_cast<const u32x4*>(zero + grp * D + 8 * c), zf);
+        const uint32_t* src = codes + grp * (int64_t)(W * D) + 8 * c;
+        uint16_t* dst = out + s * out_stride + (int64_t)g * G * D + 8 * c;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const u32x4 lo = *reinterpret_cast<const u32x4*>(src + w * D);
+            const u32x4 hi = *reinterpret_cast<const u32x4*>(src + w * D + 4);
+            const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int t = w * PER + i;
+                if (t < nv) {
+                    uint32_t o[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t q0 = (wd[2 * k] >> (i * BITS)) & kMask;
+                        const uint32_t q1 = (wd[2 * k + 1] >> (i * BITS)) & kMask;
+                        o[k] = pack2(dequant1(q0, sf[2 * k], zf[2 * k]),
+                                     dequant1(q1, sf[2 * k + 1], zf[2 * k + 1]));
+                    }
+                    __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]},
+                                                reinterpret_cast<u32x4*>(dst + (int64_t)t * D));
+                }
+            }
+        }
+    }
+}
+
+// Values: lane c of a token row owns channels 8c..8c+7.
+template <int BITS, int G>
+__global__ void __launch_bounds__(kBlock)
+decode_v_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
+                const uint16_t* __restrict__ zero, int n_tokens, int D, int lpt_log2,
+                int rows_per_block, int blocks_per_slice, int64_t n_blocks, int cap, int ngv,
+                uint16_t* __restrict__ out, int64_t out_stride) {
+    constexpr int GL = G / 8;
+    constexpr uint32_t kMask = (1u << BITS) - 1u;
+    const int lpt = 1 << lpt_log2;
+    const int c = threadIdx.x & (lpt - 1);
+    const int r0 = threadIdx.x >> lpt_log2;
+    const int rstep = kBlock >> lpt_log2;
+    if (c >= (D >> 3)) return;
+    const int wpt = ngv * G * BITS / 32;
+    const int gi = c / GL;
+    for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+        const int64_t s = blk / blocks_per_slice;
+        const int tb = (int)(blk - s * blocks_per_slice) * rows_per_block;
+        for (int r = r0; r < rows_per_block; r += rstep) {
+            const int t = tb + r;
+            if (t >= n_tokens) break;
+            const int64_t row = s * cap + t;
+            const uint32_t* rc = codes + row * wpt;
+            uint32_t q[8];
+            if (BITS == 4) {
+                const uint32_t w = rc[c];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) q[i] = (w >> (4 * i)) & kMask;
+            } else if (BITS == 8) {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(rc + 2 * c);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    q[i] = (w.x >> (8 * i)) & kMask;
+                    q[4 + i] = (w.y >> (8 * i)) & kMask;
+                }
+            } else {
+                const uint32_t w = rc[c >> 1] >> ((c & 1) * 16);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) q[i] = (w >> (2 * i)) & kMask;
+            }
+            const float sc = (float)__builtin_bit_cast(f16, scale[row * ngv + gi]);
+            const float zr = (float)__builtin_bit_cast(f16, zero[row * ngv + gi]);
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                o[k] = pack2(dequant1(q[2 * k], sc, zr), dequant1(q[2 * k + 1], sc, zr));
+            __builtin_nontemporal_store(
+                u32x4{o[0], o[1], o[2], o[3]},
+                reinterpret_cast<u32x4*>(out + s * out_stride + (int64_t)t * D + 8 * c));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// streaming: append one token per slice, optionally flush the oldest G
+// ---------------------------------------------------------------------------
+
+// Residual token i (0 = oldest) of slice s before the step: the new token
+// when i == ring_count (it is written to the ring by this same launch),
+// otherwise ring slot (head + i) mod slots.
+__device__ __forceinline__ const uint16_t* residual_token(const uint16_t* ring, const uint16_t* fresh,
+                                                          int64_t s, int i, int head, int count,
+                                                          int slots, int D) {
+    if (i == count) return fresh + s * D;
+    int slot = head + i;
+    if (slot >= slots) slot -= slots;
+    return ring + (s * slots + slot) * (int64_t)D;
+}
+
+template <int BITS, int G>
+__device__ void flush_keys(const StepArgs& a, int tpb, int64_t kblk, u32x4* lds4) {
+    const int D = a.head_dim;
+    const int half_d = D >> 1;
+    const int cpr = D >> 3;
+    const int tid = threadIdx.x;
+    // stage tpb tiles (slices kblk*tpb + ti), G residual tokens each
+    const int rows = tpb * G;
+    const int cc = tid % cpr;
+    const int r0 = tid / cpr;
+    const int rstep = kBlock / cpr;
+    for (int row = r0; row < rows; row += rstep) {
+        const int ti = row / G;
+        const int i = row - ti * G;
+        const int64_t s = kblk * tpb + ti;
+        if (s < a.n_slices) {
+            const uint16_t* src = residual_token(a.k_ring, a.k_new, s, i, a.ring_head, a.ring_count,
+                                                 a.ring_slots, D);
+            lds4[row * cpr + cc] = *reinterpret_cast<const u32x4*>(src + 8 * cc);
+        }
+    }
+    __syncthreads();
+    const int ti = tid / half_d;
+    const int p = tid - ti * half_d;
+    const int64_t s = kblk * tpb + ti;
+    if (ti < tpb && s < a.n_slices) {
+        const int out_groups = a.cap_tokens / G;
+        const int64_t grp = s * out_groups + a.n_quant / G;
+        const uint32_t* col = reinterpret_cast<const uint32_t*>(lds4) + ti * G * half_d + p;
+        key_column<BITS, G, true>(col, half_d, G, D, p, grp, a.k_codes, a.k_scale, a.k_zero);
+    }
+}
+
+template <int BITS, int G>
+__device__ void flush_values(const StepArgs& a, int64_t vblk, int lpt_log2) {
+    constexpr int GL = G / 8;
+    const int D = a.head_dim;
+    const int lpt = 1 << lpt_log2;
+    const int c = threadIdx.x & (lpt - 1);
+    const int rpb = kBlock >> lpt_log2;          // rows per block
+    const int64_t flat = vblk * rpb + (threadIdx.x >> lpt_log2);
+    const int64_t s = flat / G;
+    const int i = (int)(flat - s * G);
+    const bool rvalid = s < a.n_slices;
+    const bool cvalid = c < (D >> 3);
+    const int ngv = (D + G - 1) / G;
+    const bool in_group = (c / GL) < ngv;
+    u32x4 x = u32x4{0, 0, 0, 0};
+    if (rvalid && cvalid) {
+        const uint16_t* src = residual_token(a.v_ring, a.v_new, s, i, a.ring_head, a.ring_count,
+                                             a.ring_slots, D);
+        x = *reinterpret_cast<const u32x4*>(src + 8 * c);
+    }
+    const int wpt = ngv * G * BITS / 32;
+    const int64_t row = s * a.cap_tokens + a.n_quant + i;
+    value_chunk<BITS, G>(x, cvalid, c, rvalid && in_group, a.v_codes + row * wpt,
+                         a.v_scale + row * ngv, a.v_zero + row * ngv);
+}
+
+// Block ranges: [0, nk) key flush tiles, [nk, nk + nv) value flush rows,
+// [nk + nv, nk + nv + na) append copies.  nk = nv = 0 on a step without flush.
+template <int G>
+__global__ void __launch_bounds__(kBlock)
+append_flush_kernel(StepArgs a, int tpb, int lpt_log2, int64_t nk, int64_t nv, int64_t na) {
+    extern __shared__ u32x4 lds4[];
+    const int64_t b = blockIdx.x;
+    if (b < nk) {
+        switch (a.k_bits) {
+            case 2: flush_keys<2, G>(a, tpb, b, lds4); break;
+            case 4: flush_keys<4, G>(a, tpb, b, lds4); break;
+            default: flush_keys<8, G>(a, tpb, b, lds4); break;
+        }
+        return;
+    }
+    if (b < nk + nv) {
+        switch (a.v_bits) {
+            case 2: flush_values<2, G>(a, b - nk, lpt_log2); break;
+            case 4: flush_values<4, G>(a, b - nk, lpt_log2); break;
+            default: flush_values<8, G>(a, b - nk, lpt_log2); break;
+        }
+        return;
+    }
+    // append: one 16-byte chunk per thread, keys then values
+    const int cpr = a.head_dim >> 3;
+    const int64_t per_tensor = a.n_slices * cpr;
+    const int64_t chunk = (b - nk - nv) * kBlock + threadIdx.x;
+    if (chunk >= 2 * per_tensor) return;
+    const bool is_v = chunk >= per_tensor;
+    const int64_t cidx = is_v ? chunk - per_tensor : chunk;
+    const int64_t s = cidx / cpr;
+    const int cc = (int)(cidx - s * cpr);
+    int slot = a.ring_head + a.ring_count;
+    if (slot >= a.ring_slots) slot -= a.ring_slots;
+    const uint16_t* src = (is_v ? a.v_new : a.k_new) + s * a.head_dim + 8 * cc;
+    uint16_t* dst = (is_v ? a.v_ring : a.k_ring) + (s * a.ring_slots + slot) * (int64_t)a.head_dim + 8 * cc;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+}
+
+// Prefill: copy tokens [first, first + n) of each slice into ring slots [0, n).
+__global__ void __launch_bounds__(kBlock)
+ring_fill_kernel(RingFillArgs a, int64_t per_tensor) {
+    const int cpr = a.head_dim >> 3;
+    for (int64_t chunk = (int64_t)blockIdx.x * kBlock + threadIdx.x; chunk < 2 * per_tensor;
+         chunk += (int64_t)gridDim.x * kBlock) {
+        const bool is_v = chunk >= per_tensor;
+        int64_t cidx = is_v ? chunk - per_tensor : chunk;
+        const int cc = (int)(cidx % cpr);
+        cidx /= cpr;
+        const int i = (int)(cidx % a.n_tokens);
+        const int64_t s = cidx / a.n_tokens;
+        const uint16_t* src = (is_v ? a.v_in : a.k_in) + s * a.in_stride +
+                              (int64_t)(a.first_token + i) * a.head_dim + 8 * cc;
+        uint16_t* dst = (is_v ? a.v_ring : a.k_ring) + (s * a.ring_slots + i) * (int64_t)a.head_dim + 8 * cc;
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launch geometry
+// ---------------------------------------------------------------------------
+
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+unsigned grid_for(int64_t blocks) {
+    return (unsigned)(blocks < kMaxGrid ? (blocks > 0 ? blocks : 1) : kMaxGrid);
+}
+
+// key groups staged per block: as many as keep 256 threads busy with one
+// channel pair each, within 32 KiB of LDS (at least one group)
+int key_tiles_per_block(int G, int D) {
+    int t = (2 * kBlock) / D;
+    const int lds_cap = 16384 / (G * D);
+    if (lds_cap < t) t = lds_cap;
+    return t < 1 ? 1 : t;
+}
+
+// lanes per token row for the value kernels: a power of two covering both the
+// row's 8-channel chunks and one whole value group
+int value_lanes_log2(int G, int D) {
+    int need = D / 8;
+    if (G / 8 > need) need = G / 8;
+    int l = 0;
+    while ((1 << l) < need) ++l;
+    return l;
+}
+
+constexpr int kValueRowsPerBlock = 64;
+
+template <int BITS, int G>
+int run_encode_k(const EncodeArgs& a, hipStream_t st) {
+    const int D = a.head_dim;
+    const int ng = (a.n_tokens + G - 1) / G;
+    const int tpb = key_tiles_per_block(G, D);
+    const int bps = (ng + tpb - 1) / tpb;
+    const int64_t nb = a.n_slices * bps;
+    const size_t lds = (size_t)tpb * G * D * sizeof(uint16_t);
+    const int out_groups = (a.cap_tokens + G - 1) / G;
+    hipLaunchKernelGGL((encode_k_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), lds, st, a.in,
+                       a.in_stride, a.n_tokens, D, ng, tpb, bps, nb, a.codes, a.scale, a.zero,
+                       out_groups);
+    return (int)hipGetLastError();
+}
+
+template <int BITS, int G>
+int run_encode_v(const EncodeArgs& a, hipStream_t st) {
+    const int D = a.head_dim;
+    const int l2 = value_lanes_log2(G, D);
+    const int bps = (a.n_tokens + kValueRowsPerBlock - 1) / kValueRowsPerBlock;
+    const int64_t nb = a.n_slices * bps;
+    const int ngv = (D + G - 1) / G;
+    hipLaunchKernelGGL((encode_v_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), 0, st, a.in,
+                       a.in_stride, a.n_tokens, D, l2, kValueRowsPerBlock, bps, nb, a.codes, a.scale,
+                       a.zero, a.cap_tokens, ngv);
+    return (int)hipGetLastError();
+}
+
+template <int BITS, int G>
+int run_decode_k(const DecodeArgs& a, hipStream_t st) {
+    const int D = a.head_dim;
+    const int ng = (a.n_tokens + G - 1) / G;
+    const int tiles_pb = kBlock / (D / 8);
+    const int64_t n_tiles = a.n_slices * ng;
+    const int64_t nb = ceil_div64(n_tiles, tiles_pb);
+    const int out_groups = (a.cap_tokens + G - 1) / G;
+    hipLaunchKernelGGL((decode_k_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), 0, st, a.codes,
+                       a.scale, a.zero, a.n_tokens, D, ng, out_groups, tiles_pb, n_tiles, nb, a.out,
+                       a.out_stride);
+    return (int)hipGetLastError();
+}
+
+template <int BITS, int G>
+int run_decode_v(const DecodeArgs& a, hipStream_t st) {
+    const int D = a.head_dim;
+    const int l2 = value_lanes_log2(G, D);
+    const int bps = (a.n_tokens + kValueRowsPerBlock - 1) / kValueRowsPerBlock;
+    const int64_t nb = a.n_slices * bps;
+    const int ngv = (D + G - 1) / G;
+    hipLaunchKernelGGL((decode_v_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), 0, st, a.codes,
+                       a.scale, a.zero, a.n_tokens, D, l2, kValueRowsPerBlock, bps, nb, a.cap_tokens,
+                       ngv, a.out, a.out_stride);
+    return (int)hipGetLastError();
+}
+
+template <int G>
+int run_append_flush(const StepArgs& a, hipStream_t st) {
+    const int D = a.head_dim;
+    const int tpb = key_tiles_per_block(G, D);
+    const int l2 = value_lanes_log2(G, D);
+    const int64_t nk = a.flush ? ceil_div64(a.n_slices, tpb) : 0;
+    const int64_t nv = a.flush ? ceil_div64(a.n_slices * G, kBlock >> l2) : 0;
+    const int64_t na = ceil_div64(2 * a.n_slices * (D / 8), kBlock);
+    const size_t lds = a.flush ? (size_t)tpb * G * D * sizeof(uint16_t) : 0;
+    const int64_t total = nk + nv + na;
+    if (total > 0x7FFFFFFF) return (int)hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((append_flush_kernel<G>), dim3((unsigned)total), dim3(kBlock), lds, st, a, tpb,
+                       l2, nk, nv, na);
+    return (int)hipGetLastError();
+}
+
+#define KIVI_DISPATCH(RUN)                                                   \
+    switch (a.group_size) {                                                  \
+        case 32:                                                             \
+            return a.bits == 2 ? RUN<2, 32>(a, st)                           \
+                   : a.bits == 4 ? RUN<4, 32>(a, st) : RUN<8, 32>(a, st);    \
+        case 64:                                                             \
+            return a.bits == 2 ? RUN<2, 64>(a, st)                           \
+                   : a.bits == 4 ? RUN<4, 64>(a, st) : RUN<8, 64>(a, st);    \
+        default:                                                             \
+            return a.bits == 2 ? RUN<2, 128>(a, st)                          \
+                   : a.bits == 4 ? RUN<4, 128>(a, st) : RUN<8, 128>(a, st);  \
+    }
+
+}  // namespace
+
+int launch_encode_k(const EncodeArgs& a, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    KIVI_DISPATCH(run_encode_k)
+}
+
+int launch_encode_v(const EncodeArgs& a, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    KIVI_DISPATCH(run_encode_v)
+}
+
+int launch_decode_k(const DecodeArgs& a, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    KIVI_DISPATCH(run_decode_k)
+}
+
+int launch_decode_v(const DecodeArgs& a, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    KIVI_DISPATCH(run_decode_v)
+}
+
+int launch_append_flush(const StepArgs& a, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    switch (a.group_size) {
+        case 32: return run_append_flush<32>(a, st);
+        case 64: return run_append_flush<64>(a, st);
+        default: return run_append_flush<128>(a, st);
+    }
+}
+
+int launch_ring_fill(const RingFillArgs& a, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t per_tensor = a.n_slices * (int64_t)a.n_tokens * (a.head_dim / 8);
+    const int64_t nb = ceil_div64(2 * per_tensor, kBlock);
+    hipLaunchKernelGGL(ring_fill_kernel, dim3(grid_for(nb)), dim3(kBlock), 0, st, a, per_tensor);
+    return (int)hipGetLastError();
+}
+
+}  // namespace kivi

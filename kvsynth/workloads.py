@@ -197,11 +197,13 @@ def uniform_with_ties(S: int, T: int, D: int, *, axis: str, n_valid: int,
     for p in picks:
         if axis == "token":
             s, g, d = groups[p]
-            idx = [(s, t, d) for t in range(g * G, min((g + 1) * G, n_valid))]
+            t0, t1 = g * G, min((g + 1) * G, n_valid)
+            view = x[s, t0:t1, d]
         else:
             s, t, g = groups[p]
-            idx = [(s, t, c) for c in range(g * G, min((g + 1) * G, D))]
-        n = len(idx)
+            c0, c1 = g * G, min((g + 1) * G, D)
+            view = x[s, t, c0:c1]
+        n = view.shape[0]
         if n < 3:
             continue
         step = s_max / (2 ** int(rng.integers(0, 3)))
@@ -213,9 +215,7 @@ def uniform_with_ties(S: int, T: int, D: int, *, axis: str, n_valid: int,
         vals[order[0]] = m
         vals[order[1]] = m + levels * step
         n_ties = max(1, int(round(tie_fraction_in_group * n)))
-        for j in order[2:2 + n_ties]:
-            k = int(rng.integers(0, levels))
-            vals[j] = m + (k + 0.5) * step
-        for (a, b, c), val in zip(idx, vals):
-            x[a, b, c] = val
+        ks = rng.integers(0, levels, size=n_ties)
+        vals[order[2:2 + n_ties]] = (m + (ks + 0.5) * step).astype(np.float16)
+        view[:] = vals
     return x
