@@ -76,6 +76,9 @@ __device__ __forceinline__ QParams make_params(float mn, float mx, uint32_t& sca
     constexpr double kInvLevels = 1.0 / (double)((1 << BITS) - 1);
     mn = mn + 0.0f;                       // -0 -> +0 (round-to-nearest)
     mx = mx + 0.0f;
+    // Keep both canonical values: otherwise (-y + 0) - mn may be rewritten as
+    // -y - mn, which yields -0 for an all-zero group.
+    asm volatile("" : "+v"(mn), "+v"(mx));
     const float rng = mx - mn;
     float s32 = (float)((double)rng * kInvLevels);
     asm volatile("" : "+v"(s32));

@@ -145,7 +145,8 @@ def dequantize(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray) -> np.nda
     z32 = np.asarray(zero).astype(F32)
     y = (q32 * s32).astype(F32)
     y = (y + z32).astype(F32)
-    return y.astype(F16)
+    with np.errstate(over="ignore"):      # |y| >= 65520 rounds to +-inf, as IEEE says
+        return y.astype(F16)
 
 
 # ---------------------------------------------------------------------------

@@ -9,7 +9,7 @@ import torch
 import kv_cache_quantization_codec_amd as K
 from oracle import kivi_ref as ref
 
-POISON32 = 0x5A5A5A5A - (1 << 32)     # as a signed int32
+POISON32 = 0x5A5A5A5A                 # fits a signed int32
 POISON16 = 0x5A5A                     # an ordinary fp16 value (203.25)
 
 
