@@ -98,6 +98,26 @@ def cpu_baseline(k, v, w, cfg, n, budget_s=12.0):
     }
 
 
+def copy_ceiling(dev, nbytes=1 << 32, reps=10):
+    """Read+write GB/s of torch's device copy kernel over ``nbytes``: the
+    practical streaming ceiling, and the calibration kernel for HBM counters."""
+    import torch
+
+    src = torch.empty(nbytes // 2, dtype=torch.float16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return round(2 * nbytes / (ms / 1000.0) / 1e9, 1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +127,8 @@ def main():
                     choices=["llama2_7b_2bit", "mistral_7b_k2v4", "single_layer_4bit"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="also time a plain 4 GiB device-to-device copy (read + write)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this codec benchmark runs on one GPU only; "
@@ -211,6 +233,8 @@ def main():
             "algorithmic_bytes_per_launch": alg[dom],
         },
     }
+    if args.copy_ceiling:
+        out["copy_ceiling_GBps"] = copy_ceiling(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(k, v, w, cfg, n, args.cpu_budget)
     print(json.dumps(out), flush=True)

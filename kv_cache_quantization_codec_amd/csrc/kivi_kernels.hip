@@ -60,6 +60,8 @@ struct QParams {
     float zero;     // the group minimum, +0 for a zero of either sign
     float scale;    // fp16 scale widened to fp32
     float rcp;      // ~1/scale (within 1 ulp), 0 when scale == 0
+    float nzr;      // -fp32(zero * rcp)
+    bool fast;      // the fast path below is exact for this group
 };
 
 // Statistics -> parameters.  mn/mx are fp16 values held in fp32 (exact).
@@ -87,29 +89,66 @@ __device__ __forceinline__ QParams make_params(float mn, float mx, uint32_t& sca
     p.scale = (float)sh;
     p.zero = mn;
     p.rcp = (p.scale == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(p.scale);
+    const float zr = mn * p.rcp;
+    p.nzr = -zr;
+    p.fast = (p.scale >= 0x1p-14f) && (__builtin_fabsf(zr) <= 1024.0f);
     scale_bits = __builtin_bit_cast(uint16_t, sh);
     zero_bits = __builtin_bit_cast(uint16_t, (f16)mn);
     return p;
 }
 
-// Code of one element.  Fast path: y = d * rcp, which differs from the exact
-// fp32 quotient Q = fp32(d / scale) by at most 2^-22 * Q (1-ulp reciprocal
-// plus two roundings), i.e. by at most 2^-14 for Q <= 256.  Unless y lies
-// within 2^-12 of a half-integer, rint(y) == rint(Q); inside that band the
-// IEEE division is done (correctly rounded: no fast-math).  Values above the
-// top level are clamped; y >= 2^b - 1 already implies clamp(rint(Q)) = 2^b-1.
+// Code of one element by the definition: IEEE fp32 division (correctly
+// rounded: no fast-math), round half to even, clamp; 0 when scale == 0.
 template <int BITS>
-__device__ __forceinline__ uint32_t quant1(float x, const QParams& p) {
+__device__ __forceinline__ uint32_t quant_exact(float x, const QParams& p) {
     constexpr float kTop = (float)((1 << BITS) - 1);
     const float d = x - p.zero;
-    const float y = d * p.rcp;
-    const float yc = __builtin_fminf(y, kTop);
-    const float r = __builtin_rintf(yc);
+    const float q = __builtin_fminf(__builtin_rintf(d / p.scale), kTop);
+    return (p.scale == 0.0f) ? 0u : (uint32_t)q;
+}
+
+// Fast path for groups with p.fast: y = fp32(x * rcp - zr) in one fma (x is
+// the fp16 input, widened inside the instruction).  Let q = (x - zero)/s be
+// the exact quotient.  A normal fp16 scale s is within 2^-11 (relative) of
+// (mx - mn)/(2^b - 1), so 0 <= q <= (2^b - 1)(1 + 2^-10) < 256.  Error terms:
+// the final rounding of y, 2^-24|y| <= 2^-16; zr = fp32(zero*rcp) with
+// |zr| <= 2^10, 2^-14; rcp within 1 ulp (2^-23 relative) of 1/s, 2^-23 q <=
+// 2^-15.  The definition's Q = fp32(fp32(x - zero)/s) is within 2^-23 q of
+// q.  So |y - Q| <= 0.57 * 2^-12: rint(y) == rint(Q) unless y lies within
+// 2^-12 of a half-integer, where the exact path decides, and rint(y) never
+// exceeds 2^b - 1, so no clamp is needed.
+template <int BITS>
+__device__ __forceinline__ uint32_t quant_fast(float x, const QParams& p) {
+    const float y = __builtin_fmaf(x, p.rcp, p.nzr);
+    const float r = __builtin_rintf(y);
     uint32_t q = (uint32_t)r;
-    if (__builtin_fabsf(yc - r) > 0.5f - 0x1p-12f) {
-        q = (uint32_t)__builtin_fminf(__builtin_rintf(d / p.scale), kTop);
-    }
+    if (__builtin_fabsf(y - r) > 0.5f - 0x1p-12f) q = quant_exact<BITS>(x, p);
     return q;
+}
+
+// Codes of N elements x(i) of one group.  Fast groups take a branch-free
+// pass that also records the largest |y - rint(y)|; only when some element
+// came within 2^-12 of a half-integer (rare) is the pass redone with the
+// per-element check of quant_fast.
+template <int BITS, int N, typename X>
+__device__ __forceinline__ void quant_n(X x, const QParams& p, uint32_t* q) {
+    if (p.fast) {
+        float worst = 0.0f;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const float y = __builtin_fmaf(x(i), p.rcp, p.nzr);
+            const float r = __builtin_rintf(y);
+            q[i] = (uint32_t)r;
+            worst = __builtin_fmaxf(worst, __builtin_fabsf(y - r));
+        }
+        if (worst > 0.5f - 0x1p-12f) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) q[i] = quant_fast<BITS>(x(i), p);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) q[i] = quant_exact<BITS>(x(i), p);
+    }
 }
 
 // fp16 of fp32(q * scale + zero); q * scale is exact in fp32, so the fma
@@ -122,23 +161,26 @@ __device__ __forceinline__ f16 dequant1(uint32_t q, float scale, float zero) {
 }
 
 // ---------------------------------------------------------------------------
-// keys: one channel pair of one tile (G tokens x D channels) staged in LDS
+// keys: one channel pair of one key group (G tokens) per thread
 // ---------------------------------------------------------------------------
 
-// Quantizes channels 2p, 2p+1 of one key group from LDS column `col` (dword
-// stride `half_d`) with `nv` valid tokens, and stores its W code words per
+// Quantizes channels 2p, 2p+1 of one key group, whose token t (as an fp16
+// pair) `load(t)` returns, with `nv` valid tokens, and stores its W code words per
 // channel and both sidecars.  `grp` is the group's index in the (slice,
-// group) output arrays.
-template <int BITS, int G, bool FULL>
-__device__ __forceinline__ void key_column(const uint32_t* col, int half_d, int nv, int D, int p,
-                                           int64_t grp, uint32_t* __restrict__ codes,
+// group) output arrays.  Both channels are quantized in one pass over the
+// tokens and packed as they go, so only the staged values stay live; the
+// pass is redone with per-element checks only when some element came within
+// 2^-12 of a rounding tie (see quant_fast).
+template <int BITS, int G, bool FULL, typename Load>
+__device__ __forceinline__ void key_column(Load load, int nv, int D, int p, int64_t grp,
+                                           uint32_t* __restrict__ codes,
                                            uint16_t* __restrict__ scale,
                                            uint16_t* __restrict__ zero) {
     constexpr int W = G * BITS / 32;
     constexpr int PER = 32 / BITS;
     uint32_t v[G];
 #pragma unroll
-    for (int t = 0; t < G; ++t) v[t] = col[(FULL ? t : (t < nv ? t : nv - 1)) * half_d];
+    for (int t = 0; t < G; ++t) v[t] = load(FULL ? t : (t < nv ? t : nv - 1));
     f16x2 mn = as_h2(v[0]), mx = mn;
 #pragma unroll
     for (int t = 1; t < G; ++t) {
@@ -154,16 +196,42 @@ __device__ __forceinline__ void key_column(const uint32_t* col, int half_d, int 
         w0[w] = 0;
         w1[w] = 0;
     }
+    bool redo = !(p0.fast && p1.fast);
+    if (!redo) {
+        float worst = 0.0f;
 #pragma unroll
-    for (int t = 0; t < G; ++t) {
-        uint32_t q0 = quant1<BITS>(lo_f32(v[t]), p0);
-        uint32_t q1 = quant1<BITS>(hi_f32(v[t]), p1);
-        if (!FULL && t >= nv) {
-            q0 = 0;
-            q1 = 0;
+        for (int t = 0; t < G; ++t) {
+            const float y0 = __builtin_fmaf(lo_f32(v[t]), p0.rcp, p0.nzr);
+            const float y1 = __builtin_fmaf(hi_f32(v[t]), p1.rcp, p1.nzr);
+            const float r0 = __builtin_rintf(y0);
+            const float r1 = __builtin_rintf(y1);
+            worst = __builtin_fmaxf(worst, __builtin_fmaxf(__builtin_fabsf(y0 - r0),
+                                                           __builtin_fabsf(y1 - r1)));
+            const uint32_t c0 = (!FULL && t >= nv) ? 0u : (uint32_t)r0;
+            const uint32_t c1 = (!FULL && t >= nv) ? 0u : (uint32_t)r1;
+            w0[t / PER] |= c0 << ((t % PER) * BITS);
+            w1[t / PER] |= c1 << ((t % PER) * BITS);
         }
-        w0[t / PER] |= q0 << ((t % PER) * BITS);
-        w1[t / PER] |= q1 << ((t % PER) * BITS);
+        redo = worst > 0.5f - 0x1p-12f;
+    }
+    if (redo) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            w0[w] = 0;
+            w1[w] = 0;
+        }
+#pragma unroll
+        for (int t = 0; t < G; ++t) {
+            const float x0 = lo_f32(v[t]), x1 = hi_f32(v[t]);
+            uint32_t c0 = p0.fast ? quant_fast<BITS>(x0, p0) : quant_exact<BITS>(x0, p0);
+            uint32_t c1 = p1.fast ? quant_fast<BITS>(x1, p1) : quant_exact<BITS>(x1, p1);
+            if (!FULL && t >= nv) {
+                c0 = 0;
+                c1 = 0;
+            }
+            w0[t / PER] |= c0 << ((t % PER) * BITS);
+            w1[t / PER] |= c1 << ((t % PER) * BITS);
+        }
     }
     uint32_t* cdst = codes + grp * (int64_t)(W * D) + 2 * p;
 #pragma unroll
@@ -172,53 +240,70 @@ __device__ __forceinline__ void key_column(const uint32_t* col, int half_d, int 
     *reinterpret_cast<uint32_t*>(zero + grp * D + 2 * p) = zb0 | (zb1 << 16);
 }
 
-// Full-cache key encode.  A block stages `tpb` consecutive groups of one slice
-// (tpb*G tokens x D channels, contiguous in HBM) into LDS with 16-byte loads;
-// thread (ti, p) then owns channel pair p of group ti for all G tokens.
+// Buffer resource over `bytes` bytes at `base` (raw buffer, no stride).  Loads
+// through it take the wave-uniform part of the address in scalar registers,
+// so per-load address arithmetic costs no vector instructions.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+constexpr int kNontemporal = 2;   // buffer-load cache policy: streaming, do not keep
+
+// Full-cache key encode, full groups.  Thread (ti, p) of a block owns channel
+// pair p of key group g0 + ti of one slice, for all G tokens of the group:
+// token t is one dword, and the lanes of a wave read whole token rows (D/2
+// consecutive dwords, 256 bytes at D = 128), so every load is coalesced.  The
+// G values stay in registers for the statistics and the codes.  (Staging the
+// tile in LDS with 16-byte loads, or with direct-to-LDS loads, measured
+// slower: each lane needs its whole column in registers anyway.)  The
+// partial last group of each slice is left to encode_k_tail_kernel, so this
+// loop has no bounds logic at all.
 template <int BITS, int G>
 __global__ void __launch_bounds__(kBlock)
-encode_k_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int n_tokens, int D, int ng,
-                int tpb, int batches_per_slice, int64_t n_batches, uint32_t* __restrict__ codes,
+encode_k_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int D, int ng_full, int tpb,
+                int batches_per_slice, int64_t n_batches, uint32_t* __restrict__ codes,
                 uint16_t* __restrict__ scale, uint16_t* __restrict__ zero, int out_groups) {
-    extern __shared__ u32x4 lds4[];
     const int half_d = D >> 1;
     const int tid = threadIdx.x;
     const int ti = tid / half_d;
     const int p = tid - ti * half_d;
-    const uint32_t* lds = reinterpret_cast<const uint32_t*>(lds4);
+    if (ti >= tpb) return;
+    const int voff = (ti * G * D + 2 * p) * 2;          // bytes from the batch base
+    const int row_bytes = D * 2;
     for (int64_t batch = blockIdx.x; batch < n_batches; batch += gridDim.x) {
         const int64_t s = batch / batches_per_slice;
         const int g0 = (int)(batch - s * batches_per_slice) * tpb;
-        const int t0 = g0 * G;
-        const int nt = min(tpb * G, n_tokens - t0);
-        const u32x4* src = reinterpret_cast<const u32x4*>(in + s * in_stride + (int64_t)t0 * D);
-        const int nchunks = nt * (D >> 3);
-        __syncthreads();
-        for (int base = 0; base < nchunks; base += 8 * kBlock) {
-            u32x4 r[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int c = base + j * kBlock + tid;
-                if (c < nchunks) r[j] = __builtin_nontemporal_load(src + c);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int c = base + j * kBlock + tid;
-                if (c < nchunks) lds4[c] = r[j];
-            }
-        }
-        __syncthreads();
         const int g = g0 + ti;
-        if (ti < tpb && g < ng) {
-            const int nv = min(G, n_tokens - g * G);
-            const uint32_t* col = lds + ti * G * half_d + p;
-            const int64_t grp = s * out_groups + g;
-            if (nv == G)
-                key_column<BITS, G, true>(col, half_d, nv, D, p, grp, codes, scale, zero);
-            else
-                key_column<BITS, G, false>(col, half_d, nv, D, p, grp, codes, scale, zero);
-        }
+        if (g >= ng_full) continue;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            buffer_rsrc(in + s * in_stride + (int64_t)g0 * G * D, (uint32_t)(tpb * G * row_bytes));
+        auto load = [&](int t) {
+            return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, voff, t * row_bytes,
+                                                                   kNontemporal);
+        };
+        key_column<BITS, G, true>(load, G, D, p, s * out_groups + g, codes, scale, zero);
     }
+}
+
+// The partial last key group (n_tokens % G valid tokens) of every slice.
+template <int BITS, int G>
+__global__ void __launch_bounds__(kBlock)
+encode_k_tail_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int n_tokens, int D,
+                     int64_t n_slices, uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
+                     uint16_t* __restrict__ zero, int out_groups) {
+    const int half_d = D >> 1;
+    const int tpb = kBlock / half_d;
+    const int ti = threadIdx.x / half_d;
+    const int p = threadIdx.x - ti * half_d;
+    const int64_t s = (int64_t)blockIdx.x * tpb + ti;
+    if (ti >= tpb || s >= n_slices) return;
+    const int g = n_tokens / G;
+    const int nv = n_tokens - g * G;
+    const uint32_t* col =
+        reinterpret_cast<const uint32_t*>(in + s * in_stride + (int64_t)g * G * D) + p;
+    auto load = [&](int t) { return col[t * half_d]; };
+    key_column<BITS, G, false>(load, nv, D, p, s * out_groups + g, codes, scale, zero);
 }
 
 // ---------------------------------------------------------------------------
@@ -230,7 +315,7 @@ encode_k_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int n_tokens
 // of the wave must call this together (DPP reductions inside).  Stores the
 // row's code words and, from the first lane of each group, its sidecars,
 // when `store` is set.
-template <int BITS, int G>
+template <int BITS, int G, bool ALL = false>
 __device__ __forceinline__ void value_chunk(const u32x4& x, bool cvalid, int c, bool store,
                                             uint32_t* __restrict__ row_codes,
                                             uint16_t* __restrict__ row_scale,
@@ -241,7 +326,7 @@ __device__ __forceinline__ void value_chunk(const u32x4& x, bool cvalid, int c, 
     const f16x2 mx2 = pmax(pmax(a0, a1), pmax(a2, a3));
     f16 mn = mn2.x < mn2.y ? mn2.x : mn2.y;
     f16 mx = mx2.x > mx2.y ? mx2.x : mx2.y;
-    if (!cvalid) {
+    if (!ALL && !cvalid) {
         mn = (f16)__builtin_inff();
         mx = (f16)(-__builtin_inff());
     }
@@ -259,12 +344,8 @@ __device__ __forceinline__ void value_chunk(const u32x4& x, bool cvalid, int c, 
     const QParams prm = make_params<BITS>((float)pr.x, -(float)pr.y, sb, zb);
     const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
     uint32_t q[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        q[2 * i] = quant1<BITS>(lo_f32(xs[i]), prm);
-        q[2 * i + 1] = quant1<BITS>(hi_f32(xs[i]), prm);
-    }
-    if (!cvalid) {
+    quant_n<BITS, 8>([&](int i) { return (i & 1) ? hi_f32(xs[i >> 1]) : lo_f32(xs[i >> 1]); }, prm, q);
+    if (!ALL && !cvalid) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = 0;
     }
@@ -292,7 +373,9 @@ __device__ __forceinline__ void value_chunk(const u32x4& x, bool cvalid, int c, 
 
 // Full-cache value encode: a block covers `rows_per_block` token rows of one
 // slice; 2^lpt_log2 lanes per row.
-template <int BITS, int G>
+// ALL: every lane of a row holds 8 real channels that belong to a stored
+// group (D/8 is the lane count and G divides D), so no padding logic.
+template <int BITS, int G, bool ALL>
 __global__ void __launch_bounds__(kBlock)
 encode_v_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int n_tokens, int D,
                 int lpt_log2, int rows_per_block, int blocks_per_slice, int64_t n_blocks,
@@ -303,8 +386,8 @@ encode_v_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int n_tokens
     const int c = threadIdx.x & (lpt - 1);
     const int r0 = threadIdx.x >> lpt_log2;
     const int rstep = kBlock >> lpt_log2;
-    const bool cvalid = c < (D >> 3);
-    const bool in_group = (c / GL) < ngv;
+    const bool cvalid = ALL || c < (D >> 3);
+    const bool in_group = ALL || (c / GL) < ngv;
     const int wpt = ngv * G * BITS / 32;
     for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
         const int64_t s = blk / blocks_per_slice;
@@ -317,8 +400,8 @@ encode_v_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int n_tokens
             if (rvalid && cvalid)
                 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)t * D + 8 * c));
             const int64_t row = s * cap + t;
-            value_chunk<BITS, G>(x, cvalid, c, rvalid && in_group, codes + row * wpt,
-                                 scale + row * ngv, zero + row * ngv);
+            value_chunk<BITS, G, ALL>(x, cvalid, c, rvalid && in_group, codes + row * wpt,
+                                      scale + row * ngv, zero + row * ngv);
         }
     }
 }
@@ -344,7 +427,43 @@ __device__ __forceinline__ uint32_t pack2(f16 a, f16 b) {
 }
 
 // Keys: lane c of a tile owns channels 8c..8c+7 of one group for all its
-// tokens; per token it writes 16 bytes of the token-major output.
+// tokens; per token it writes 16 bytes of the token-major output.  Full groups
+// (all but a slice's last) take a path without conditions.
+template <int BITS, int G, bool FULL>
+__device__ __forceinline__ void decode_k_group(const uint32_t* __restrict__ src,
+                                               const uint16_t* __restrict__ sc16,
+                                               const uint16_t* __restrict__ zr16, int nv, int D,
+                                               uint16_t* __restrict__ dst) {
+    constexpr int W = G * BITS / 32;
+    constexpr int PER = 32 / BITS;
+    constexpr uint32_t kMask = (1u << BITS) - 1u;
+    float sf[8], zf[8];
+    widen8(*reinterpret_cast<const u32x4*>(sc16), sf);
+    widen8(*reinterpret_cast<const u32x4*>(zr16), zf);
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(src + w * D);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(src + w * D + 4);
+        const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int t = w * PER + i;
+            if (FULL || t < nv) {
+                uint32_t o[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t q0 = (wd[2 * k] >> (i * BITS)) & kMask;
+                    const uint32_t q1 = (wd[2 * k + 1] >> (i * BITS)) & kMask;
+                    o[k] = pack2(dequant1(q0, sf[2 * k], zf[2 * k]),
+                                 dequant1(q1, sf[2 * k + 1], zf[2 * k + 1]));
+                }
+                __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]},
+                                            reinterpret_cast<u32x4*>(dst + (int64_t)t * D));
+            }
+        }
+    }
+}
+
 template <int BITS, int G>
 __global__ void __launch_bounds__(kBlock)
 decode_k_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
@@ -352,8 +471,6 @@ decode_k_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__
                 int tiles_per_block, int64_t n_tiles, int64_t n_blocks, uint16_t* __restrict__ out,
                 int64_t out_stride) {
     constexpr int W = G * BITS / 32;
-    constexpr int PER = 32 / BITS;
-    constexpr uint32_t kMask = (1u << BITS) - 1u;
     const int cpr = D >> 3;
     const int ti = threadIdx.x / cpr;
     const int c = threadIdx.x - ti * cpr;
@@ -365,87 +482,97 @@ decode_k_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__
         const int g = (int)(tile - s * ng);
         const int nv = min(G, n_tokens - g * G);
         const int64_t grp = s * out_groups + g;
-        float sf[8], zf[8];
-        widen8(*reinterpret_cast<const u32x4*>(scale + grp * D + 8 * c), sf);
-        widen8(*reinterpret_cast<const u32x4*>(zero + grp * D + 8 * c), zf);
         const uint32_t* src = codes + grp * (int64_t)(W * D) + 8 * c;
+        const uint16_t* sc = scale + grp * D + 8 * c;
+        const uint16_t* zr = zero + grp * D + 8 * c;
         uint16_t* dst = out + s * out_stride + (int64_t)g * G * D + 8 * c;
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(src + w * D);
-            const u32x4 hi = *reinterpret_cast<const u32x4*>(src + w * D + 4);
-            const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int t = w * PER + i;
-                if (t < nv) {
-                    uint32_t o[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t q0 = (wd[2 * k] >> (i * BITS)) & kMask;
-                        const uint32_t q1 = (wd[2 * k + 1] >> (i * BITS)) & kMask;
-                        o[k] = pack2(dequant1(q0, sf[2 * k], zf[2 * k]),
-                                     dequant1(q1, sf[2 * k + 1], zf[2 * k + 1]));
-                    }
-                    __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]},
-                                                reinterpret_cast<u32x4*>(dst + (int64_t)t * D));
-                }
-            }
-        }
+        if (nv == G)
+            decode_k_group<BITS, G, true>(src, sc, zr, nv, D, dst);
+        else
+            decode_k_group<BITS, G, false>(src, sc, zr, nv, D, dst);
     }
 }
 
-// Values: lane c of a token row owns channels 8c..8c+7.
+constexpr int kRowsPerThread = 4;
+
+// Values: lane c of a token row owns channels 8c..8c+7; each thread loads the
+// codes and sidecars of its kRowsPerThread rows before decoding them.  Blocks
+// whose rows are all valid (all but the last block of a slice) run without
+// any condition, so the scheduler can issue every load before the first use.
+template <int BITS, int G, bool FULL>
+__device__ __forceinline__ void decode_v_rows(const uint32_t* __restrict__ codes,
+                                              const uint16_t* __restrict__ scale,
+                                              const uint16_t* __restrict__ zero, int64_t s,
+                                              int tb, int rstep, int n_tokens, int D, int c,
+                                              int cap, int ngv, uint16_t* __restrict__ out,
+                                              int64_t out_stride) {
+    constexpr int GL = G / 8;
+    constexpr uint32_t kMask = (1u << BITS) - 1u;
+    const int wpt = ngv * G * BITS / 32;
+    const int gi = c / GL;
+    u32x2 wd[kRowsPerThread];
+    float sc[kRowsPerThread], zr[kRowsPerThread];
+#pragma unroll
+    for (int j = 0; j < kRowsPerThread; ++j) {
+        // past the end, re-read the last row (not stored)
+        const int t = FULL ? tb + j * rstep : min(tb + j * rstep, n_tokens - 1);
+        const int64_t row = s * cap + t;
+        const uint32_t* rc = codes + row * wpt;
+        if (BITS == 8) {
+            wd[j] = *reinterpret_cast<const u32x2*>(rc + 2 * c);
+        } else {
+            wd[j].x = (BITS == 4) ? rc[c] : (rc[c >> 1] >> ((c & 1) * 16));
+            wd[j].y = 0;
+        }
+        sc[j] = (float)__builtin_bit_cast(f16, scale[row * ngv + gi]);
+        zr[j] = (float)__builtin_bit_cast(f16, zero[row * ngv + gi]);
+    }
+#pragma unroll
+    for (int j = 0; j < kRowsPerThread; ++j) {
+        const int t = tb + j * rstep;
+        uint32_t q[8];
+        if (BITS == 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                q[i] = (wd[j].x >> (8 * i)) & kMask;
+                q[4 + i] = (wd[j].y >> (8 * i)) & kMask;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = (wd[j].x >> (BITS * i)) & kMask;
+        }
+        uint32_t o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            o[k] = pack2(dequant1(q[2 * k], sc[j], zr[j]), dequant1(q[2 * k + 1], sc[j], zr[j]));
+        if (FULL || t < n_tokens)
+            __builtin_nontemporal_store(
+                u32x4{o[0], o[1], o[2], o[3]},
+                reinterpret_cast<u32x4*>(out + s * out_stride + (int64_t)t * D + 8 * c));
+    }
+}
+
 template <int BITS, int G>
 __global__ void __launch_bounds__(kBlock)
 decode_v_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scale,
                 const uint16_t* __restrict__ zero, int n_tokens, int D, int lpt_log2,
-                int rows_per_block, int blocks_per_slice, int64_t n_blocks, int cap, int ngv,
+                int blocks_per_slice, int64_t n_blocks, int cap, int ngv,
                 uint16_t* __restrict__ out, int64_t out_stride) {
-    constexpr int GL = G / 8;
-    constexpr uint32_t kMask = (1u << BITS) - 1u;
     const int lpt = 1 << lpt_log2;
     const int c = threadIdx.x & (lpt - 1);
     const int r0 = threadIdx.x >> lpt_log2;
     const int rstep = kBlock >> lpt_log2;
+    const int rows_per_block = kRowsPerThread * rstep;
     if (c >= (D >> 3)) return;
-    const int wpt = ngv * G * BITS / 32;
-    const int gi = c / GL;
     for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
         const int64_t s = blk / blocks_per_slice;
-        const int tb = (int)(blk - s * blocks_per_slice) * rows_per_block;
-        for (int r = r0; r < rows_per_block; r += rstep) {
-            const int t = tb + r;
-            if (t >= n_tokens) break;
-            const int64_t row = s * cap + t;
-            const uint32_t* rc = codes + row * wpt;
-            uint32_t q[8];
-            if (BITS == 4) {
-                const uint32_t w = rc[c];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) q[i] = (w >> (4 * i)) & kMask;
-            } else if (BITS == 8) {
-                const u32x2 w = *reinterpret_cast<const u32x2*>(rc + 2 * c);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    q[i] = (w.x >> (8 * i)) & kMask;
-                    q[4 + i] = (w.y >> (8 * i)) & kMask;
-                }
-            } else {
-                const uint32_t w = rc[c >> 1] >> ((c & 1) * 16);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) q[i] = (w >> (2 * i)) & kMask;
-            }
-            const float sc = (float)__builtin_bit_cast(f16, scale[row * ngv + gi]);
-            const float zr = (float)__builtin_bit_cast(f16, zero[row * ngv + gi]);
-            uint32_t o[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                o[k] = pack2(dequant1(q[2 * k], sc, zr), dequant1(q[2 * k + 1], sc, zr));
-            __builtin_nontemporal_store(
-                u32x4{o[0], o[1], o[2], o[3]},
-                reinterpret_cast<u32x4*>(out + s * out_stride + (int64_t)t * D + 8 * c));
-        }
+        const int row0 = (int)(blk - s * blocks_per_slice) * rows_per_block;
+        if (row0 + rows_per_block <= n_tokens)
+            decode_v_rows<BITS, G, true>(codes, scale, zero, s, row0 + r0, rstep, n_tokens, D, c,
+                                         cap, ngv, out, out_stride);
+        else
+            decode_v_rows<BITS, G, false>(codes, scale, zero, s, row0 + r0, rstep, n_tokens, D, c,
+                                          cap, ngv, out, out_stride);
     }
 }
 
@@ -465,41 +592,41 @@ __device__ __forceinline__ const uint16_t* residual_token(const uint16_t* ring, 
     return ring + (s * slots + slot) * (int64_t)D;
 }
 
+// Key flush: thread (ti, p) quantizes channel pair p of slice kblk*tpb + ti
+// from the oldest G residual tokens.  The ring slot of residual token t is
+// the same for every slice, so it is a scalar offset of a buffer load.
 template <int BITS, int G>
-__device__ void flush_keys(const StepArgs& a, int tpb, int64_t kblk, u32x4* lds4) {
+__device__ __forceinline__ void flush_keys(const StepArgs& a, int tpb, int64_t kblk) {
     const int D = a.head_dim;
     const int half_d = D >> 1;
-    const int cpr = D >> 3;
     const int tid = threadIdx.x;
-    // stage tpb tiles (slices kblk*tpb + ti), G residual tokens each
-    const int rows = tpb * G;
-    const int cc = tid % cpr;
-    const int r0 = tid / cpr;
-    const int rstep = kBlock / cpr;
-    for (int row = r0; row < rows; row += rstep) {
-        const int ti = row / G;
-        const int i = row - ti * G;
-        const int64_t s = kblk * tpb + ti;
-        if (s < a.n_slices) {
-            const uint16_t* src = residual_token(a.k_ring, a.k_new, s, i, a.ring_head, a.ring_count,
-                                                 a.ring_slots, D);
-            lds4[row * cpr + cc] = *reinterpret_cast<const u32x4*>(src + 8 * cc);
-        }
-    }
-    __syncthreads();
     const int ti = tid / half_d;
     const int p = tid - ti * half_d;
-    const int64_t s = kblk * tpb + ti;
-    if (ti < tpb && s < a.n_slices) {
-        const int out_groups = a.cap_tokens / G;
-        const int64_t grp = s * out_groups + a.n_quant / G;
-        const uint32_t* col = reinterpret_cast<const uint32_t*>(lds4) + ti * G * half_d + p;
-        key_column<BITS, G, true>(col, half_d, G, D, p, grp, a.k_codes, a.k_scale, a.k_zero);
-    }
+    const int64_t s0 = kblk * tpb;
+    const int64_t s = s0 + ti;
+    if (ti >= tpb || s >= a.n_slices) return;
+    const int row_bytes = D * 2;
+    const int64_t nblk = (a.n_slices - s0 < tpb) ? a.n_slices - s0 : tpb;
+    const __amdgpu_buffer_rsrc_t ring = buffer_rsrc(
+        a.k_ring + s0 * a.ring_slots * (int64_t)D, (uint32_t)(nblk * a.ring_slots * row_bytes));
+    const __amdgpu_buffer_rsrc_t fresh =
+        buffer_rsrc(a.k_new + s0 * (int64_t)D, (uint32_t)(nblk * row_bytes));
+    const int ring_off = (ti * a.ring_slots * D + 2 * p) * 2;
+    const int new_off = (ti * D + 2 * p) * 2;
+    auto load = [&](int t) {
+        if (t == a.ring_count)      // the token appended by this same launch
+            return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(fresh, new_off, 0, 0);
+        int slot = a.ring_head + t;
+        if (slot >= a.ring_slots) slot -= a.ring_slots;
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ring, ring_off, slot * row_bytes, 0);
+    };
+    const int out_groups = a.cap_tokens / G;
+    key_column<BITS, G, true>(load, G, D, p, s * out_groups + a.n_quant / G, a.k_codes,
+                              a.k_scale, a.k_zero);
 }
 
 template <int BITS, int G>
-__device__ void flush_values(const StepArgs& a, int64_t vblk, int lpt_log2) {
+__device__ __forceinline__ void flush_values(const StepArgs& a, int64_t vblk, int lpt_log2) {
     constexpr int GL = G / 8;
     const int D = a.head_dim;
     const int lpt = 1 << lpt_log2;
@@ -529,13 +656,12 @@ __device__ void flush_values(const StepArgs& a, int64_t vblk, int lpt_log2) {
 template <int G>
 __global__ void __launch_bounds__(kBlock)
 append_flush_kernel(StepArgs a, int tpb, int lpt_log2, int64_t nk, int64_t nv, int64_t na) {
-    extern __shared__ u32x4 lds4[];
     const int64_t b = blockIdx.x;
     if (b < nk) {
         switch (a.k_bits) {
-            case 2: flush_keys<2, G>(a, tpb, b, lds4); break;
-            case 4: flush_keys<4, G>(a, tpb, b, lds4); break;
-            default: flush_keys<8, G>(a, tpb, b, lds4); break;
+            case 2: flush_keys<2, G>(a, tpb, b); break;
+            case 4: flush_keys<4, G>(a, tpb, b); break;
+            default: flush_keys<8, G>(a, tpb, b); break;
         }
         return;
     }
@@ -592,17 +718,12 @@ unsigned grid_for(int64_t blocks) {
     return (unsigned)(blocks < kMaxGrid ? (blocks > 0 ? blocks : 1) : kMaxGrid);
 }
 
-// key groups staged per block: as many as keep 256 threads busy with one
-// channel pair each, within 32 KiB of LDS (at least one group)
-int key_tiles_per_block(int G, int D) {
-    int t = (2 * kBlock) / D;
-    const int lds_cap = 16384 / (G * D);
-    if (lds_cap < t) t = lds_cap;
-    return t < 1 ? 1 : t;
-}
+// key groups per block: as many as keep 256 threads busy with one channel
+// pair each
+int key_tiles_per_block(int D) { return (2 * kBlock) / D; }
 
 // lanes per token row for the value kernels: a power of two covering both the
-// row's 8-channel chunks and one whole value group
+// row's 8-channel chunks and one whole value group (G/8 lanes)
 int value_lanes_log2(int G, int D) {
     int need = D / 8;
     if (G / 8 > need) need = G / 8;
@@ -616,15 +737,25 @@ constexpr int kValueRowsPerBlock = 64;
 template <int BITS, int G>
 int run_encode_k(const EncodeArgs& a, hipStream_t st) {
     const int D = a.head_dim;
-    const int ng = (a.n_tokens + G - 1) / G;
-    const int tpb = key_tiles_per_block(G, D);
-    const int bps = (ng + tpb - 1) / tpb;
-    const int64_t nb = a.n_slices * bps;
-    const size_t lds = (size_t)tpb * G * D * sizeof(uint16_t);
+    const int ng_full = a.n_tokens / G;
+    const int tpb = key_tiles_per_block(D);
     const int out_groups = (a.cap_tokens + G - 1) / G;
-    hipLaunchKernelGGL((encode_k_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), lds, st, a.in,
-                       a.in_stride, a.n_tokens, D, ng, tpb, bps, nb, a.codes, a.scale, a.zero,
-                       out_groups);
+    if (ng_full > 0) {
+        const int bps = (ng_full + tpb - 1) / tpb;
+        const int64_t nb = a.n_slices * bps;
+        hipLaunchKernelGGL((encode_k_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), 0, st,
+                           a.in, a.in_stride, D, ng_full, tpb, bps, nb, a.codes, a.scale, a.zero,
+                           out_groups);
+        const int err = (int)hipGetLastError();
+        if (err) return err;
+    }
+    if (a.n_tokens % G) {
+        const int64_t nb = ceil_div64(a.n_slices, tpb);
+        if (nb > 0x7FFFFFFF) return (int)hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((encode_k_tail_kernel<BITS, G>), dim3((unsigned)nb), dim3(kBlock), 0,
+                           st, a.in, a.in_stride, a.n_tokens, D, a.n_slices, a.codes, a.scale,
+                           a.zero, out_groups);
+    }
     return (int)hipGetLastError();
 }
 
@@ -635,9 +766,15 @@ int run_encode_v(const EncodeArgs& a, hipStream_t st) {
     const int bps = (a.n_tokens + kValueRowsPerBlock - 1) / kValueRowsPerBlock;
     const int64_t nb = a.n_slices * bps;
     const int ngv = (D + G - 1) / G;
-    hipLaunchKernelGGL((encode_v_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), 0, st, a.in,
-                       a.in_stride, a.n_tokens, D, l2, kValueRowsPerBlock, bps, nb, a.codes, a.scale,
-                       a.zero, a.cap_tokens, ngv);
+    const bool all = (1 << l2) == D / 8 && D % G == 0;
+    if (all)
+        hipLaunchKernelGGL((encode_v_kernel<BITS, G, true>), dim3(grid_for(nb)), dim3(kBlock), 0,
+                           st, a.in, a.in_stride, a.n_tokens, D, l2, kValueRowsPerBlock, bps, nb,
+                           a.codes, a.scale, a.zero, a.cap_tokens, ngv);
+    else
+        hipLaunchKernelGGL((encode_v_kernel<BITS, G, false>), dim3(grid_for(nb)), dim3(kBlock), 0,
+                           st, a.in, a.in_stride, a.n_tokens, D, l2, kValueRowsPerBlock, bps, nb,
+                           a.codes, a.scale, a.zero, a.cap_tokens, ngv);
     return (int)hipGetLastError();
 }
 
@@ -659,27 +796,27 @@ template <int BITS, int G>
 int run_decode_v(const DecodeArgs& a, hipStream_t st) {
     const int D = a.head_dim;
     const int l2 = value_lanes_log2(G, D);
-    const int bps = (a.n_tokens + kValueRowsPerBlock - 1) / kValueRowsPerBlock;
+    const int rpb = kRowsPerThread * (kBlock >> l2);
+    const int bps = (a.n_tokens + rpb - 1) / rpb;
     const int64_t nb = a.n_slices * bps;
     const int ngv = (D + G - 1) / G;
     hipLaunchKernelGGL((decode_v_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), 0, st, a.codes,
-                       a.scale, a.zero, a.n_tokens, D, l2, kValueRowsPerBlock, bps, nb, a.cap_tokens,
-                       ngv, a.out, a.out_stride);
+                       a.scale, a.zero, a.n_tokens, D, l2, bps, nb, a.cap_tokens, ngv, a.out,
+                       a.out_stride);
     return (int)hipGetLastError();
 }
 
 template <int G>
 int run_append_flush(const StepArgs& a, hipStream_t st) {
     const int D = a.head_dim;
-    const int tpb = key_tiles_per_block(G, D);
+    const int tpb = key_tiles_per_block(D);
     const int l2 = value_lanes_log2(G, D);
     const int64_t nk = a.flush ? ceil_div64(a.n_slices, tpb) : 0;
     const int64_t nv = a.flush ? ceil_div64(a.n_slices * G, kBlock >> l2) : 0;
     const int64_t na = ceil_div64(2 * a.n_slices * (D / 8), kBlock);
-    const size_t lds = a.flush ? (size_t)tpb * G * D * sizeof(uint16_t) : 0;
     const int64_t total = nk + nv + na;
     if (total > 0x7FFFFFFF) return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((append_flush_kernel<G>), dim3((unsigned)total), dim3(kBlock), lds, st, a, tpb,
+    hipLaunchKernelGGL((append_flush_kernel<G>), dim3((unsigned)total), dim3(kBlock), 0, st, a, tpb,
                        l2, nk, nv, na);
     return (int)hipGetLastError();
 }
