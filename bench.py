@@ -48,19 +48,21 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch measured with rocprofv3 counters for this kernel
-    source, read from profiles/traffic_<workload>.json (None when absent or
-    taken on another version of the kernels)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    """HBM bytes per launch of ``kernel`` measured with rocprofv3 counters and
+    scaled by a copy of known size (profiles/traffic_<workload>.txt), or None
+    when no such record exists or it was taken on another kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
-    try:
-        rec = json.load(open(path))
-    except ValueError:
-        return None
+    rec = {}
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if "=" in line:
+            key, val = (x.strip() for x in line.split("=", 1))
+            rec[key] = val
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch", {}).get(kernel)
+    return int(rec[kernel]) if kernel in rec else None
 
 
 def cpu_baseline(k, v, w, cfg, n, budget_s=12.0):

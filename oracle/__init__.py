@@ -14,15 +14,15 @@ Two tiers, written independently of each other and of the HIP path:
 Sources (titles of the pages the method is taken from):
 
 * CacheForge README, "How it works": keys are quantized per channel, values
-  per token, the most recent tokens are kept at higher precision; the
+  per token, and the newest tokens are not quantized; the
   "Example" section names the knobs ``k_bits``, ``v_bits``, ``group_size``
   and ``residual_length`` (recent fp16 tokens), defaults 2/2/32/128.
 * CacheSeek pull request #4 "Feature(quantization): add KIVI KV-cache
   quantization for exact-prefix reuse", description: KIVI encode/decode with
   grouped statistics, padding, and packing of the codes into int32 words;
   compact ``qdata``/``scale``/``offset`` payload.
-* vLLM ``turboquant/config.py``, ``TurboQuantConfig`` docstring ("3 = 8
-  levels, 4 = 16 levels": b bits give 2**b levels) and ``value_packed_size``
+* vLLM ``turboquant/config.py``, ``TurboQuantConfig`` docstring (a b-bit
+  code has 2**b levels, stated there for 3 and 4 bits) and ``value_packed_size``
   (a per-vector uniform value code costs ceil(D*b/8) bytes plus an fp16
   scale and an fp16 zero).
 

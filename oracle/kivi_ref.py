@@ -7,12 +7,12 @@ fusion; a Python loop over groups, numpy arithmetic inside each group.
 Method (CacheForge README, "How it works"; CacheSeek PR #4 description):
 
 * keys   -- one (scale, zero) pair per channel per group of ``G`` consecutive
-  tokens ("per-channel" key quantization);
+  tokens (keys are quantized channel by channel);
 * values -- one (scale, zero) pair per token per group of ``G`` consecutive
-  channels ("per-token" value quantization);
+  channels (values are quantized token by token);
 * codes of ``b`` bits (2**b levels, vLLM ``TurboQuantConfig`` docstring),
-  packed into 32-bit words ("int4 packing to int32", CacheSeek PR #4), with
-  padding for partial groups;
+  packed into 32-bit words (CacheSeek PR #4 packs 4-bit codes into int32),
+  with padding for partial groups;
 * the most recent ``R`` tokens stay in fp16 (CacheForge README, "How it
   works" and the ``residual_length`` knob in "Example").
 
