@@ -120,13 +120,106 @@ def copy_ceiling(dev, nbytes=1 << 32, reps=10):
     return round(2 * nbytes / (ms / 1000.0) / 1e9, 1)
 
 
+def stream_bench(w, args):
+    """Streaming decode: prefill, then w.steps calls of kivi_append_flush (one
+    launch each, all slices of all layers); per-step GPU time from HIP events
+    on the launch stream."""
+    import numpy as np
+    import torch
+
+    import kv_cache_quantization_codec_amd as K
+    from kvsynth import layer_kv, stream_tokens
+
+    cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
+    S, T, D, G = w.slices, w.tokens, w.head_dim, w.group_size
+    dev = torch.device("cuda:0")
+    k = torch.empty((S, T, D), dtype=torch.float16, device=dev)
+    v = torch.empty_like(k)
+    spl = w.slices_per_layer
+    for layer in range(w.layers):
+        kl, vl = layer_kv(w, layer, device=dev)
+        k[layer * spl:(layer + 1) * spl] = kl
+        v[layer * spl:(layer + 1) * spl] = vl
+        del kl, vl
+    kn, vn = stream_tokens(w, w.steps, device=dev)
+    cap = -(-(T + w.steps) // G) * G
+
+    def run(record):
+        st = K.Stream(cfg, S, cap, dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        K.kivi_stream_prefill(st, k, v, T)
+        e1.record()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(w.steps + 1)]
+        flushed = []
+        ev[0].record()
+        for i in range(w.steps):
+            flushed.append(K.kivi_append_flush(st, kn[i], vn[i]))
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        step_us = [ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(w.steps)]
+        return e0.elapsed_time(e1), step_us, flushed, st
+
+    for _ in range(max(args.warmup, 1)):
+        run(False)
+    t0 = time.perf_counter()
+    prefill_ms, step_us, flushed, st = run(True)
+    wall = time.perf_counter() - t0
+    fl = np.array([u for u, f in zip(step_us, flushed) if f])
+    nf = np.array([u for u, f in zip(step_us, flushed) if not f])
+    allv = np.array(step_us)
+    nq = (T - w.residual_length) // G * G
+    prefill_bytes = (algorithmic_bytes("k", "encode", S, nq, D, G, w.k_bits)
+                     + algorithmic_bytes("v", "encode", S, nq, D, G, w.v_bits)
+                     + 2 * S * (T - nq) * D * 2 * 2)
+    # every step: read k_new and v_new, write both into the rings, and write
+    # the new value row's codes and sidecars (values are quantized on arrival);
+    # a flush step also encodes one key group (read G ring rows, write codes)
+    ngv = -(-D // G)
+    append_bytes = (2 * 2 * S * D * 2
+                    + S * (ngv * (G * w.v_bits // 32) * 4 + 2 * ngv * 2))
+    flush_bytes = algorithmic_bytes("k", "encode", S, G, D, G, w.k_bits)
+    pct = lambda a, q: round(float(np.percentile(a, q)), 2) if len(a) else None
+    return {
+        "metric": "streaming decode step latency (append 1 token per slice; flush a group "
+                  "when the fp16 residual exceeds R), 1 MI355X",
+        "value": pct(allv, 50),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": w.steps,
+        "warmup": max(args.warmup, 1),
+        "ms_per_step": round(float(allv.mean()) / 1000.0, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.batch, "kv_heads": w.heads,
+                   "head_dim": D, "prefill_tokens": T, "k_bits": w.k_bits, "v_bits": w.v_bits,
+                   "group_size": G, "residual_length": w.residual_length},
+        "p99_us": pct(allv, 99),
+        "flush_steps": int(len(fl)),
+        "flush_p50_us": pct(fl, 50), "flush_p99_us": pct(fl, 99),
+        "append_p50_us": pct(nf, 50), "append_p99_us": pct(nf, 99),
+        "append_GBps": round(append_bytes / (float(np.median(nf)) * 1e-6) / 1e9, 1) if len(nf) else None,
+        "flush_GBps": round((append_bytes + flush_bytes) / (float(np.median(fl)) * 1e-6) / 1e9, 1)
+        if len(fl) else None,
+        "prefill_ms": round(prefill_ms, 3),
+        "prefill_GBps": round(prefill_bytes / (prefill_ms * 1e-3) / 1e9, 1),
+        "host_wall_steps_per_s": round(w.steps / wall, 1),
+        "final_state": {"n_quant": st.n_quant, "residual": st.ring_count},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama2_7b_2bit",
-                    choices=["llama2_7b_2bit", "mistral_7b_k2v4", "single_layer_4bit"])
+                    choices=["llama2_7b_2bit", "mistral_7b_k2v4", "single_layer_4bit",
+                             "stream_b64"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-ceiling", action="store_true",
@@ -146,6 +239,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     K.binding.lib()
     w = WORKLOADS[args.workload]
+    if w.steps:
+        print(json.dumps(stream_bench(w, args)), flush=True)
+        return
     cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
     S, T, D, G = w.slices, w.tokens, w.head_dim, w.group_size
     n = T - w.residual_length

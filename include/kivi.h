@@ -175,6 +175,11 @@ int kivi_decode_v(const kivi_config* cfg, const int32_t* codes,
  *       fp16 [n_slices][R + G][D]: the fp16 residual of each slice as a
  *       ring; residual token i (0 = oldest) sits in slot
  *       (ring_head + i) mod (R + G).
+ * Value groups are per token, so a value row is quantized as soon as its
+ * token arrives (by the prefill or by the step that appends it): store rows
+ * n_quant .. n_quant + ring_count - 1 (those below cap_tokens) already hold
+ * the codes of the residual tokens.  Only rows below n_quant are part of the
+ * quantized prefix; readers take the residual from the fp16 ring.
  * Host counters (owned by the caller, updated by the library):
  *   n_slices    slices in every array.
  *   cap_tokens  quantized-token capacity, a multiple of G.

@@ -247,7 +247,12 @@ int kivi_stream_prefill(const kivi_config* cfg, kivi_stream* st, const void* k, 
             s = kivi_encode_k(cfg, k, st->n_slices, nq, in_stride, st->cap_tokens, st->k_codes,
                               st->k_scale, st->k_zero, stream);
             if (s) return s;
-            s = kivi_encode_v(cfg, v, st->n_slices, nq, in_stride, st->cap_tokens, st->v_codes,
+        }
+        // value rows are per token: the residual's rows are quantized now too
+        // (up to the capacity), as kivi_append_flush does for each new token
+        const int64_t nv = n_tokens < st->cap_tokens ? n_tokens : st->cap_tokens;
+        if (nv > 0) {
+            s = kivi_encode_v(cfg, v, st->n_slices, nv, in_stride, st->cap_tokens, st->v_codes,
                               st->v_scale, st->v_zero, stream);
             if (s) return s;
         }

@@ -625,37 +625,47 @@ __device__ __forceinline__ void flush_keys(const StepArgs& a, int tpb, int64_t k
                               a.k_scale, a.k_zero);
 }
 
+// Append of slice s (one token row, 2^lpt_log2 lanes of 8 channels): the new
+// key and value rows go into ring slot (head + count) mod slots, and the
+// value row is quantized at once into store row n_quant + count -- value
+// groups are per token, so a row's codes never depend on later tokens.  The
+// store therefore already holds the codes of every residual value row (rows
+// past cap_tokens are skipped: they can never be flushed); only the key
+// groups wait for a flush.
 template <int BITS, int G>
-__device__ __forceinline__ void flush_values(const StepArgs& a, int64_t vblk, int lpt_log2) {
+__device__ __forceinline__ void append_row(const StepArgs& a, int64_t ablk, int lpt_log2) {
     constexpr int GL = G / 8;
     const int D = a.head_dim;
     const int lpt = 1 << lpt_log2;
     const int c = threadIdx.x & (lpt - 1);
-    const int rpb = kBlock >> lpt_log2;          // rows per block
-    const int64_t flat = vblk * rpb + (threadIdx.x >> lpt_log2);
-    const int64_t s = flat / G;
-    const int i = (int)(flat - s * G);
-    const bool rvalid = s < a.n_slices;
+    const int64_t s0 = ablk * (kBlock >> lpt_log2) + (threadIdx.x >> lpt_log2);
+    const bool svalid = s0 < a.n_slices;
+    const int64_t s = svalid ? s0 : a.n_slices - 1;
     const bool cvalid = c < (D >> 3);
+    const int cc = cvalid ? c : 0;
+    int slot = a.ring_head + a.ring_count;
+    if (slot >= a.ring_slots) slot -= a.ring_slots;
+    const int64_t ring_row = (s * a.ring_slots + slot) * (int64_t)D;
+    const u32x4 kx = *reinterpret_cast<const u32x4*>(a.k_new + s * D + 8 * cc);
+    const u32x4 vx = *reinterpret_cast<const u32x4*>(a.v_new + s * D + 8 * cc);
+    if (svalid && cvalid) {
+        *reinterpret_cast<u32x4*>(a.k_ring + ring_row + 8 * c) = kx;
+        *reinterpret_cast<u32x4*>(a.v_ring + ring_row + 8 * c) = vx;
+    }
     const int ngv = (D + G - 1) / G;
     const bool in_group = (c / GL) < ngv;
-    u32x4 x = u32x4{0, 0, 0, 0};
-    if (rvalid && cvalid) {
-        const uint16_t* src = residual_token(a.v_ring, a.v_new, s, i, a.ring_head, a.ring_count,
-                                             a.ring_slots, D);
-        x = *reinterpret_cast<const u32x4*>(src + 8 * c);
-    }
     const int wpt = ngv * G * BITS / 32;
-    const int64_t row = s * a.cap_tokens + a.n_quant + i;
-    value_chunk<BITS, G>(x, cvalid, c, rvalid && in_group, a.v_codes + row * wpt,
-                         a.v_scale + row * ngv, a.v_zero + row * ngv);
+    const int32_t vrow = a.n_quant + a.ring_count;
+    const int64_t row = s * a.cap_tokens + vrow;
+    value_chunk<BITS, G>(vx, cvalid, c, svalid && in_group && vrow < a.cap_tokens,
+                         a.v_codes + row * wpt, a.v_scale + row * ngv, a.v_zero + row * ngv);
 }
 
-// Block ranges: [0, nk) key flush tiles, [nk, nk + nv) value flush rows,
-// [nk + nv, nk + nv + na) append copies.  nk = nv = 0 on a step without flush.
+// Block ranges: [0, nk) key flush tiles (nk = 0 on a step without flush),
+// [nk, nk + na) appends.
 template <int G>
 __global__ void __launch_bounds__(kBlock)
-append_flush_kernel(StepArgs a, int tpb, int lpt_log2, int64_t nk, int64_t nv, int64_t na) {
+append_flush_kernel(StepArgs a, int tpb, int lpt_log2, int64_t nk, int64_t na) {
     const int64_t b = blockIdx.x;
     if (b < nk) {
         switch (a.k_bits) {
@@ -665,28 +675,11 @@ append_flush_kernel(StepArgs a, int tpb, int lpt_log2, int64_t nk, int64_t nv, i
         }
         return;
     }
-    if (b < nk + nv) {
-        switch (a.v_bits) {
-            case 2: flush_values<2, G>(a, b - nk, lpt_log2); break;
-            case 4: flush_values<4, G>(a, b - nk, lpt_log2); break;
-            default: flush_values<8, G>(a, b - nk, lpt_log2); break;
-        }
-        return;
+    switch (a.v_bits) {
+        case 2: append_row<2, G>(a, b - nk, lpt_log2); break;
+        case 4: append_row<4, G>(a, b - nk, lpt_log2); break;
+        default: append_row<8, G>(a, b - nk, lpt_log2); break;
     }
-    // append: one 16-byte chunk per thread, keys then values
-    const int cpr = a.head_dim >> 3;
-    const int64_t per_tensor = a.n_slices * cpr;
-    const int64_t chunk = (b - nk - nv) * kBlock + threadIdx.x;
-    if (chunk >= 2 * per_tensor) return;
-    const bool is_v = chunk >= per_tensor;
-    const int64_t cidx = is_v ? chunk - per_tensor : chunk;
-    const int64_t s = cidx / cpr;
-    const int cc = (int)(cidx - s * cpr);
-    int slot = a.ring_head + a.ring_count;
-    if (slot >= a.ring_slots) slot -= a.ring_slots;
-    const uint16_t* src = (is_v ? a.v_new : a.k_new) + s * a.head_dim + 8 * cc;
-    uint16_t* dst = (is_v ? a.v_ring : a.k_ring) + (s * a.ring_slots + slot) * (int64_t)a.head_dim + 8 * cc;
-    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
 }
 
 // Prefill: copy tokens [first, first + n) of each slice into ring slots [0, n).
@@ -812,12 +805,11 @@ int run_append_flush(const StepArgs& a, hipStream_t st) {
     const int tpb = key_tiles_per_block(D);
     const int l2 = value_lanes_log2(G, D);
     const int64_t nk = a.flush ? ceil_div64(a.n_slices, tpb) : 0;
-    const int64_t nv = a.flush ? ceil_div64(a.n_slices * G, kBlock >> l2) : 0;
-    const int64_t na = ceil_div64(2 * a.n_slices * (D / 8), kBlock);
-    const int64_t total = nk + nv + na;
+    const int64_t na = ceil_div64(a.n_slices, kBlock >> l2);
+    const int64_t total = nk + na;
     if (total > 0x7FFFFFFF) return (int)hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((append_flush_kernel<G>), dim3((unsigned)total), dim3(kBlock), 0, st, a, tpb,
-                       l2, nk, nv, na);
+                       l2, nk, na);
     return (int)hipGetLastError();
 }
 
