@@ -233,11 +233,15 @@ __device__ __forceinline__ void key_column(Load load, int nv, int D, int p, int6
             w1[t / PER] |= c1 << ((t % PER) * BITS);
         }
     }
+    // streaming stores: the payload is not read again by this launch
     uint32_t* cdst = codes + grp * (int64_t)(W * D) + 2 * p;
 #pragma unroll
-    for (int w = 0; w < W; ++w) *reinterpret_cast<u32x2*>(cdst + w * D) = u32x2{w0[w], w1[w]};
-    *reinterpret_cast<uint32_t*>(scale + grp * D + 2 * p) = sb0 | (sb1 << 16);
-    *reinterpret_cast<uint32_t*>(zero + grp * D + 2 * p) = zb0 | (zb1 << 16);
+    for (int w = 0; w < W; ++w)
+        __builtin_nontemporal_store(u32x2{w0[w], w1[w]}, reinterpret_cast<u32x2*>(cdst + w * D));
+    __builtin_nontemporal_store(sb0 | (sb1 << 16),
+                                reinterpret_cast<uint32_t*>(scale + grp * D + 2 * p));
+    __builtin_nontemporal_store(zb0 | (zb1 << 16),
+                                reinterpret_cast<uint32_t*>(zero + grp * D + 2 * p));
 }
 
 // Buffer resource over `bytes` bytes at `base` (raw buffer, no stride).  Loads
@@ -353,21 +357,22 @@ __device__ __forceinline__ void value_chunk(const u32x4& x, bool cvalid, int c, 
         uint32_t w = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) w |= q[i] << (4 * i);
-        if (store) row_codes[c] = w;
+        if (store) __builtin_nontemporal_store(w, row_codes + c);
     } else if (BITS == 8) {
         const uint32_t w0 = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
         const uint32_t w1 = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-        if (store) *reinterpret_cast<u32x2*>(row_codes + 2 * c) = u32x2{w0, w1};
+        if (store)
+            __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(row_codes + 2 * c));
     } else {
         uint32_t h = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) h |= q[i] << (2 * i);
         const uint32_t nb = dpp<0xB1>(h);
-        if (store && (c & 1) == 0) row_codes[c >> 1] = h | (nb << 16);
+        if (store && (c & 1) == 0) __builtin_nontemporal_store(h | (nb << 16), row_codes + (c >> 1));
     }
     if (store && (c % GL) == 0) {
-        row_scale[c / GL] = (uint16_t)sb;
-        row_zero[c / GL] = (uint16_t)zb;
+        __builtin_nontemporal_store((uint16_t)sb, row_scale + c / GL);
+        __builtin_nontemporal_store((uint16_t)zb, row_zero + c / GL);
     }
 }
 
