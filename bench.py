@@ -65,6 +65,83 @@ def measured_traffic(kernel: str, workload: str):
     return int(rec[kernel]) if kernel in rec else None
 
 
+CODEC_KERNELS = ("encode_k", "encode_v", "decode_k", "decode_v")
+
+
+def _codec_kernel(name: str):
+    """Which codec kernel a rocprofv3 kernel name is, or None."""
+    for k in CODEC_KERNELS:
+        if f"kivi::(anonymous namespace)::{k}_kernel<" in name:
+            return k
+    return None
+
+
+def summarize_traffic(workload: str, fetch_csv: str, write_csv: str) -> str:
+    """Text of profiles/traffic_<workload>.txt from two rocprofv3 --pmc runs of
+    this script (FETCH_SIZE, then WRITE_SIZE; counter_collection CSVs).
+
+    Calibration: the set-up assembles the cache with 2 * layers device
+    copies of one layer's K or V (slices_per_layer * tokens * head_dim fp16,
+    known size); they are the widest-grid dispatches of the runtime's copy
+    kernel before the first codec kernel.  Each counter is scaled by known
+    bytes / counted KiB on those copies."""
+    import csv
+
+    from kvsynth import WORKLOADS
+    w = WORKLOADS[workload]
+    copy_bytes = w.slices_per_layer * w.tokens * w.head_dim * 2
+    n_copies = 2 * w.layers
+
+    def read(path, counter):
+        setup, per = [], {k: [] for k in CODEC_KERNELS}
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            val = float(r["Counter_Value"])
+            kern = _codec_kernel(r["Kernel_Name"])
+            if kern:
+                per[kern].append(val)
+            elif r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer") and not any(per.values()):
+                setup.append((int(r["Grid_Size"]), val))
+        widest = max((g for g, _ in setup), default=0)
+        copies = [v for g, v in setup if g == widest]
+        if len(copies) != n_copies or not all(per.values()):
+            raise SystemExit(f"{path}: expected {n_copies} set-up copies and every codec kernel, "
+                             f"found {len(copies)} copies")
+        scale = copy_bytes / (sum(copies) / len(copies) * 1024.0)
+        return scale, {k: sum(v) / len(v) for k, v in per.items()}
+
+    fs, fetch = read(fetch_csv, "FETCH_SIZE")
+    ws, write = read(write_csv, "WRITE_SIZE")
+    lines = [
+        "# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE; KiB per",
+        f"# dispatch, one --pmc pass each) for workload {workload}, each counter scaled by",
+        f"# what it reads on the {n_copies} set-up copies of {copy_bytes} bytes each way in the",
+        "# same run.  Commands, from the repository root:",
+        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_FETCH_SIZE -o run --output-format csv -- \\",
+        f"#       python -u bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline",
+        "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_WRITE_SIZE -o run --output-format csv -- \\",
+        f"#       python -u bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline",
+        f"#   python bench.py --workload {workload} --summarize-traffic \\",
+        "#       gpurun_out/pmc_FETCH_SIZE/run_counter_collection.csv \\",
+        "#       gpurun_out/pmc_WRITE_SIZE/run_counter_collection.csv",
+        "# bench.py reports these bytes only while kivi_kernels.hip hashes to the value below.",
+        f"kernel_source_sha256_16 = {kernel_source_hash()}",
+        f"fetch_scale = {fs:.4f}",
+        f"write_scale = {ws:.4f}",
+    ]
+    n = w.tokens - w.residual_length
+    for k in CODEC_KERNELS:
+        b = w.k_bits if k.endswith("k") else w.v_bits
+        alg = algorithmic_bytes(k[-1], k[:6], w.slices, n, w.head_dim, w.group_size, b)
+        fb, wb = fetch[k] * 1024.0 * fs, write[k] * 1024.0 * ws
+        lines.append(f"# {k}: fetch {fetch[k]:.0f} KiB raw -> {fb:.0f} B, write {write[k]:.0f} KiB "
+                     f"raw -> {wb:.0f} B, sum / algorithmic = {(fb + wb) / alg:.5f}")
+        lines.append(f"{k} = {fb + wb:.0f}")
+    return "\n".join(lines) + "\n"
+
+
 def cpu_baseline(k, v, w, cfg, n, budget_s=12.0):
     """Time the numpy oracle (single thread) on whole slices of the same cache
     until about ``budget_s`` seconds of CPU work; scale to fp16-eq GB/s."""
@@ -224,7 +301,17 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="also time a plain 4 GiB device-to-device copy (read + write)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.txt from two rocprofv3 --pmc "
+                         "counter_collection CSVs of this script and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        text = summarize_traffic(args.workload, *args.summarize_traffic)
+        path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.txt")
+        with open(path, "w") as f:
+            f.write(text)
+        print(text, end="")
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this codec benchmark runs on one GPU only; "
                                    "--gpus must be 1 (slices shard across GPUs with no exchange, "

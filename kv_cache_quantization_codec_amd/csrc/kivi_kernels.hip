@@ -371,8 +371,8 @@ __device__ __forceinline__ void value_chunk(const u32x4& x, bool cvalid, int c, 
         if (store && (c & 1) == 0) __builtin_nontemporal_store(h | (nb << 16), row_codes + (c >> 1));
     }
     if (store && (c % GL) == 0) {
-        __builtin_nontemporal_store((uint16_t)sb, row_scale + c / GL);
-        __builtin_nontemporal_store((uint16_t)zb, row_zero + c / GL);
+        row_scale[c / GL] = (uint16_t)sb;
+        row_zero[c / GL] = (uint16_t)zb;
     }
 }
 
@@ -584,18 +584,6 @@ decode_v_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__
 // ---------------------------------------------------------------------------
 // streaming: append one token per slice, optionally flush the oldest G
 // ---------------------------------------------------------------------------
-
-// Residual token i (0 = oldest) of slice s before the step: the new token
-// when i == ring_count (it is written to the ring by this same launch),
-// otherwise ring slot (head + i) mod slots.
-__device__ __forceinline__ const uint16_t* residual_token(const uint16_t* ring, const uint16_t* fresh,
-                                                          int64_t s, int i, int head, int count,
-                                                          int slots, int D) {
-    if (i == count) return fresh + s * D;
-    int slot = head + i;
-    if (slot >= slots) slot -= slots;
-    return ring + (s * slots + slot) * (int64_t)D;
-}
 
 // Key flush: thread (ti, p) quantizes channel pair p of slice kblk*tpb + ti
 // from the oldest G residual tokens.  The ring slot of residual token t is
