@@ -10,6 +10,8 @@ Two tiers, written independently of each other and of the HIP path:
 * :mod:`oracle.kivi_exact` -- pure Python on exact rationals with a
   hand-written round-to-nearest-even into the binary16/binary32 formats,
   for tiny inputs.  It pins the numpy tier's use of hardware rounding.
+* :mod:`oracle.attention_ref` -- float64 decode-phase attention of one query
+  token per head over the dequantized prefix plus the fp16 residual.
 
 Sources (titles of the pages the method is taken from):
 
@@ -30,4 +32,4 @@ The pages print no formula for the statistics or the rounding; the readings
 used here are stated in each function's docstring.
 """
 
-from . import kivi_ref, kivi_exact  # noqa: F401
+from . import attention_ref, kivi_exact, kivi_ref  # noqa: F401
