@@ -225,6 +225,72 @@ int kivi_stream_prefill(const kivi_config* cfg, kivi_stream* st,
 int kivi_append_flush(const kivi_config* cfg, kivi_stream* st,
                       const void* k_new_fp16, const void* v_new_fp16, void* hip_stream);
 
+/* Decode-phase attention over the quantized cache (CacheForge README,
+ * "Contribution scope": the inherited KIVI code brings the model
+ * integrations and the kernels that consume the quantized cache; "How it
+ * works": keys quantized per channel, values per token, the newest tokens in
+ * fp16).  The pages give no formula for this consumer; the library computes
+ * ordinary softmax attention of one query token per query head,
+ *     out[s][j] = sum_t softmax_t( sm_scale * q[s][j] . k_t ) * v_t,
+ * over every cached token t of slice s: the n_quant quantized tokens,
+ * dequantized as code * scale + zero (kept in fp32, not rounded to fp16),
+ * then the res_count fp16 residual tokens.  q_per_kv consecutive query
+ * heads share one KV slice (grouped-query attention; 1 = multi-head).
+ *
+ * Cache description (host struct owned by the caller; device arrays):
+ *   k_codes .. v_zero  the key/value layouts above for cap_tokens tokens per
+ *                      slice; key groups [0, NG_k(n_quant)) and value rows
+ *                      [0, n_quant) are read, nothing else.
+ *   n_quant            quantized tokens per slice, in [0, cap_tokens]; any
+ *                      count (the last key group may be partial).
+ *   res_k, res_v       fp16 residual tokens: token i (0 = oldest) of slice s
+ *                      is the D elements at s*res_slice_stride +
+ *                      ((res_head + i) mod res_slots)*D, i < res_count.
+ *                      A kivi_stream maps to res_slots = R + G, res_slice_stride
+ *                      = (R + G)*D, res_head = ring_head, res_count =
+ *                      ring_count; a full-cache encode of T tokens maps to
+ *                      res_k = k + n_quant*D with the input's slice stride
+ *                      and res_slots = res_count = T - n_quant, res_head = 0.
+ *                      May be NULL when res_count == 0. */
+typedef struct kivi_attn_cache {
+    const int32_t* k_codes;
+    const void* k_scale;
+    const void* k_zero;
+    const int32_t* v_codes;
+    const void* v_scale;
+    const void* v_zero;
+    int64_t cap_tokens;
+    int64_t n_quant;
+    const void* res_k;
+    const void* res_v;
+    int64_t res_slice_stride;
+    int64_t res_slots;
+    int64_t res_head;
+    int64_t res_count;
+} kivi_attn_cache;
+
+/* Bytes of device workspace that kivi_decode_attention needs for these
+ * sizes (0 when every slice is done in one pass and no workspace is used).
+ * The library splits long caches over several workgroups per slice and
+ * merges their partial softmax sums in a second kernel; the workspace holds
+ * those partials.  -1 on an invalid configuration or size. */
+int64_t kivi_attention_workspace_bytes(const kivi_config* cfg, int64_t n_slices,
+                                       int32_t q_per_kv, int64_t n_quant,
+                                       int64_t res_count);
+
+/* Attention of q_fp16 [n_slices][q_per_kv][D] (contiguous) over the cache,
+ * written to out_fp16 [n_slices][q_per_kv][D] (rounded to nearest fp16).
+ * Requirements beyond the codec's: head_dim a multiple of 32 and at most
+ * 128 (KIVI_E_HEAD_DIM); q_per_kv in [1, 8], n_quant + res_count >= 1,
+ * res_count <= res_slots, 0 <= res_head < res_slots, sm_scale finite and
+ * workspace_bytes >= kivi_attention_workspace_bytes(...) (KIVI_E_SHAPE);
+ * residual stride a multiple of 8 elements (KIVI_E_ALIGN).  workspace may
+ * be NULL when that size is 0.  Async on hip_stream like the codec calls. */
+int kivi_decode_attention(const kivi_config* cfg, const kivi_attn_cache* cache,
+                          int64_t n_slices, int32_t q_per_kv, const void* q_fp16,
+                          float sm_scale, void* out_fp16, void* workspace,
+                          int64_t workspace_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,12 +6,15 @@ over it.
 """
 
 from .binding import (  # noqa: E402,F401
+    AttnCache,
     Config,
     KiviError,
     Stream,
     alloc_keys,
     alloc_values,
     kivi_append_flush,
+    kivi_attention_workspace_bytes,
+    kivi_decode_attention,
     kivi_decode_k,
     kivi_decode_v,
     kivi_encode_k,

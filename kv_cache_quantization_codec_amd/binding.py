@@ -48,10 +48,21 @@ class kivi_stream(ctypes.Structure):
                 ("ring_count", ctypes.c_int64)]
 
 
+class kivi_attn_cache(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("k_zero", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+                ("cap_tokens", ctypes.c_int64), ("n_quant", ctypes.c_int64),
+                ("res_k", ctypes.c_void_p), ("res_v", ctypes.c_void_p),
+                ("res_slice_stride", ctypes.c_int64), ("res_slots", ctypes.c_int64),
+                ("res_head", ctypes.c_int64), ("res_count", ctypes.c_int64)]
+
+
 # (name, restype, argtypes) of every symbol include/kivi.h declares
 _P, _I64, _I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 _CFG = ctypes.POINTER(kivi_config)
 _ST = ctypes.POINTER(kivi_stream)
+_AC = ctypes.POINTER(kivi_attn_cache)
 SIGNATURES = [
     ("kivi_status_string", ctypes.c_char_p, [_I32]),
     ("kivi_last_hip_error", _I32, []),
@@ -67,6 +78,8 @@ SIGNATURES = [
     ("kivi_decode_v", _I32, [_CFG, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     ("kivi_stream_prefill", _I32, [_CFG, _ST, _P, _P, _I64, _I64, _P]),
     ("kivi_append_flush", _I32, [_CFG, _ST, _P, _P, _P]),
+    ("kivi_attention_workspace_bytes", _I64, [_CFG, _I64, _I32, _I64, _I64]),
+    ("kivi_decode_attention", _I32, [_CFG, _AC, _I64, _I32, _P, ctypes.c_float, _P, _P, _I64, _P]),
 ]
 
 _lib = None
@@ -276,3 +289,74 @@ def kivi_append_flush(st: Stream, k_new: torch.Tensor, v_new: torch.Tensor, stre
     _check(lib().kivi_append_flush(_cfg(st.cfg), ctypes.byref(st.state), _ptr(k_new), _ptr(v_new),
                                    _stream_ptr(stream)), "kivi_append_flush")
     return st.state.n_quant != before
+
+
+# ---------------------------------------------------------------------------
+# decode attention over the quantized cache
+# ---------------------------------------------------------------------------
+
+class AttnCache:
+    """A ``kivi_attn_cache`` plus references to the tensors it points into.
+
+    ``keys`` / ``values``: payloads laid out for ``cap_tokens`` tokens per
+    slice (as from :func:`alloc_keys` / :func:`alloc_values`); ``n_quant`` of
+    them are read.  ``res_k`` / ``res_v``: fp16 ``[S, slots, D]`` tensors (any
+    slice stride) holding the residual as a ring whose oldest token is at
+    slot ``res_head``; ``res_count`` defaults to all slots."""
+
+    def __init__(self, cfg: Config, keys, values, n_quant: int, res_k=None, res_v=None,
+                 res_head: int = 0, res_count: int | None = None):
+        D = cfg.head_dim
+        vc, vs, vz = values
+        kc, ks, kz = keys
+        cap = vc.shape[1]
+        stride, slots = 0, 0
+        if res_k is not None and res_k.shape[1] == 0:     # an empty residual
+            res_k = res_v = None
+        if res_k is not None:
+            for t, nm in ((res_k, "res_k"), (res_v, "res_v")):
+                if t.dtype != torch.float16 or t.dim() != 3 or t.shape[2] != D or t.stride(2) != 1 \
+                        or (t.shape[1] > 1 and t.stride(1) != D):
+                    raise ValueError(f"{nm}: expected float16 [S, slots, {D}] with contiguous rows")
+            if res_v.stride(0) != res_k.stride(0) or res_v.shape[1] != res_k.shape[1]:
+                raise ValueError("res_k and res_v must share slots and slice stride")
+            stride, slots = res_k.stride(0), res_k.shape[1]
+        count = slots if res_count is None else res_count
+        self.cfg = cfg
+        self._refs = (keys, values, res_k, res_v)
+        self.c = kivi_attn_cache(_ptr(kc), _ptr(ks), _ptr(kz), _ptr(vc), _ptr(vs), _ptr(vz),
+                                 cap, n_quant, _ptr(res_k), _ptr(res_v), stride, slots,
+                                 res_head, count)
+
+    @classmethod
+    def from_stream(cls, st: Stream) -> "AttnCache":
+        return cls(st.cfg, st.keys, st.values, st.n_quant, st.k_ring, st.v_ring,
+                   st.ring_head, st.ring_count)
+
+
+def kivi_attention_workspace_bytes(cfg, n_slices: int, q_per_kv: int, n_quant: int,
+                                   res_count: int) -> int:
+    return lib().kivi_attention_workspace_bytes(_cfg(cfg), n_slices, q_per_kv, n_quant, res_count)
+
+
+def kivi_decode_attention(cfg, cache: AttnCache, q: torch.Tensor, sm_scale: float,
+                          out: torch.Tensor, workspace: torch.Tensor | None = None, stream=None):
+    """Attention of ``q`` fp16 [S, q_per_kv, D] over ``cache`` into ``out``
+    (same shape).  A workspace of the size the library asks for is allocated
+    on ``q``'s device when none is given."""
+    D = cfg.head_dim
+    for t, nm in ((q, "q"), (out, "out")):
+        if t.dtype != torch.float16 or t.dim() != 3 or t.shape[2] != D or not t.is_contiguous():
+            raise ValueError(f"{nm}: expected contiguous float16 [S, q_per_kv, {D}]")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    S, r = q.shape[0], q.shape[1]
+    need = kivi_attention_workspace_bytes(cfg, S, r, cache.c.n_quant, cache.c.res_count)
+    if need < 0:
+        raise KiviError(-6, "kivi_attention_workspace_bytes")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().kivi_decode_attention(_cfg(cfg), ctypes.byref(cache.c), S, r, _ptr(q),
+                                       float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
+                                       _stream_ptr(stream)), "kivi_decode_attention")

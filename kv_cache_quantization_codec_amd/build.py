@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkivi.so")
 
-SOURCES = [os.path.join(CSRC, "kivi_api.cpp"), os.path.join(CSRC, "kivi_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "kivi_api.cpp"), os.path.join(CSRC, "kivi_kernels.hip"),
+           os.path.join(CSRC, "kivi_attention.hip")]
 
 FLAGS = [
     "--offload-arch=gfx950",
