@@ -42,6 +42,23 @@ def algorithmic_bytes(kind: str, direction: str, S: int, n: int, D: int, G: int,
     return fp16 + codes + stats
 
 
+def attention_bytes(S: int, n: int, R: int, D: int, G: int, kb: int, vb: int, r: int,
+                    n_splits: int) -> dict:
+    """Bytes one decode-attention call must move, per kernel: the packed
+    prefix (codes + sidecars, padding slots of partial key groups included),
+    the fp16 residual, q and the output; with a split plan the partial sums
+    are written by the attention kernel and read back by the merge kernel."""
+    ngk, ngv = -(-n // G), -(-D // G)
+    payload = (S * ngk * (G * kb // 32) * D * 4 + 2 * S * ngk * D * 2
+               + S * n * ngv * (G * vb // 32) * 4 + 2 * S * n * ngv * 2)
+    resid = 2 * S * R * D * 2
+    q = out = S * r * D * 2
+    if n_splits > 1:
+        partials = S * n_splits * r * (D + 2) * 4
+        return {"attention": payload + resid + q + partials, "attention_merge": partials + out}
+    return {"attention": payload + resid + q + out}
+
+
 def kernel_source_hash() -> str:
     path = os.path.join(ROOT, "kv_cache_quantization_codec_amd", "csrc", "kivi_kernels.hip")
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
@@ -140,6 +157,89 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str) -> str:
                      f"raw -> {wb:.0f} B, sum / algorithmic = {(fb + wb) / alg:.5f}")
         lines.append(f"{k} = {fb + wb:.0f}")
     return "\n".join(lines) + "\n"
+
+
+def attention_bench(w, cfg, k, v, kq, vq, n, args, dev):
+    """Decode attention of one query token per query head over the cache
+    just encoded (quantized prefix + the R fp16 tokens left in k/v), all
+    slices in one call; HIP events on the launch stream."""
+    import torch
+
+    import kv_cache_quantization_codec_amd as K
+    from kvsynth import decode_queries
+
+    S, D, G, r = w.slices, w.head_dim, w.group_size, w.q_per_kv
+    R = w.tokens - n
+    q = decode_queries(w, dev)
+    out = torch.empty_like(q)
+    cache = K.AttnCache(cfg, kq, vq, n, k[:, n:], v[:, n:], 0, R)
+    ws_bytes = K.kivi_attention_workspace_bytes(cfg, S, r, n, R)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    sm_scale = D ** -0.5
+
+    def call():
+        K.kivi_decode_attention(cfg, cache, q, sm_scale, out, ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    reps = max(10, args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n_splits = ws_bytes // (S * r * (D + 2) * 4) if ws_bytes else 1
+    alg = attention_bytes(S, n, R, D, G, w.k_bits, w.v_bits, r, n_splits)
+    total = sum(alg.values())
+    gbps = total / (ms / 1000.0) / 1e9
+    res = {
+        "what": "softmax attention of one query token per query head over the packed prefix "
+                "plus the fp16 residual, all layers' slices in one call",
+        "q_per_kv": r,
+        "cached_tokens": w.tokens,
+        "n_splits": n_splits,
+        "ms": round(ms, 4),
+        "algorithmic_bytes": total,
+        "achieved_GBps": round(gbps, 1),
+        "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "fp16_cache_equiv_GBps": round(2 * S * w.tokens * D * 2 / (ms / 1000.0) / 1e9, 1),
+        "decode_steps_per_s": round(1000.0 / ms, 1),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = attention_cpu_baseline(w, k, v, kq, vq, q, n, sm_scale, alg,
+                                                     min(args.cpu_budget, 6.0))
+    return res
+
+
+def attention_cpu_baseline(w, k, v, kq, vq, q, n, sm_scale, alg, budget_s):
+    """The float64 attention oracle, single-threaded, on whole slices of the
+    same cache until about ``budget_s`` seconds; scaled to algorithmic GB/s."""
+    import numpy as np
+
+    from oracle import attention_ref as att
+
+    S = w.slices
+    done, spent, chunk = 0, 0.0, 4
+    while spent < budget_s and done < S:
+        sl = slice(done, min(done + chunk, S))
+        kp = tuple(t[sl].cpu().numpy() for t in kq)
+        vp = tuple(t[sl].cpu().numpy() for t in vq)
+        qh, rk, rv = q[sl].cpu().numpy(), k[sl, n:].cpu().numpy(), v[sl, n:].cpu().numpy()
+        t0 = time.perf_counter()
+        att.decode_attention(qh, kp, vp, n, rk, rv, w.k_bits, w.v_bits, w.group_size, sm_scale)
+        spent += time.perf_counter() - t0
+        done = sl.stop
+    per_slice = sum(alg.values()) / S
+    return {
+        "value": round(per_slice * done / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} of {S} slices, float64 numpy attention oracle, {spent:.1f} s single-threaded",
+    }
 
 
 def cpu_baseline(k, v, w, cfg, n, budget_s=12.0):
@@ -418,6 +518,7 @@ def main():
             "algorithmic_bytes_per_launch": alg[dom],
         },
     }
+    out["attention"] = attention_bench(w, cfg, k, v, kq, vq, n, args, dev)
     if args.copy_ceiling:
         out["copy_ceiling_GBps"] = copy_ceiling(dev)
     if not args.no_cpu_baseline:

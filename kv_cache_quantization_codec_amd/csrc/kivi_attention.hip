@@ -48,8 +48,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kMaxD = 128;
-constexpr int kAqStride = kMaxD + 8;      // halves per row of the q*s operand
 constexpr int kTokStride = 32 + 8;        // halves per row of a 32-token operand
 constexpr int kVcStride = 32 + 4;         // words per transposed value-code column
 constexpr float kNegInf = -__builtin_inff();
@@ -110,8 +108,19 @@ __device__ __forceinline__ h8 codes8(const u32x4& lo, const u32x4& hi, const Cod
     return __builtin_bit_cast(h8, r);
 }
 
+// A wave's LDS instructions execute in program order, so one wave sharing
+// data through LDS needs no s_barrier (nor the fence of __syncthreads, which
+// would also wait for the global loads kept in flight across a block); this
+// only stops the compiler from moving LDS accesses across the point.
+__device__ __forceinline__ void lds_order() { __asm__ __volatile__("" ::: "memory"); }
+
 __device__ __forceinline__ uint32_t pack_h2(f16 a, f16 b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// 16-byte LDS read as an MFMA operand.
+__device__ __forceinline__ h8 lds_h8(const void* p) {
+    return __builtin_bit_cast(h8, *reinterpret_cast<const u32x4*>(p));
 }
 
 // fp32 x as fp16 hi + lo with hi = fp16(x), lo = fp16(x - hi); x - hi is
@@ -121,30 +130,35 @@ __device__ __forceinline__ void split_hl(float x, f16& hi, f16& lo) {
     lo = (f16)(x - (float)hi);
 }
 
-template <int KB, int VB>
-struct Smem {
-    f16 aq[16][kAqStride];                 // q*s of the current key group, hi/lo rows
-    f16 kz[kMaxD];                         // zeros of the current key group
-    uint32_t kc[KB][kMaxD];                // key codes of a 32-token block
-    uint32_t vc[VB * kMaxD / 32][kVcStride];  // value codes, [word column][row]
+// LDS of one wave (D = head_dim).  Row strides are padded by 16 bytes so
+// that the 16 rows an MFMA operand read touches fall in different banks.
+template <int KB, int VB, int D>
+struct alignas(16) Smem {
+    f16 q[8][D + 8];                       // the slice's queries, one row per head
+    f16 aq[16][D + 8];                     // q*s of the current key group, hi/lo rows
+    f16 kz[D];                             // zeros of the current key group
+    uint32_t kc[KB][D];                    // key codes of a 32-token block
+    uint32_t vc[VB * D / 32][kVcStride];   // value codes, [word column][row]
     f16 vz[4][kTokStride];                 // value zeros, [group][row]
-    float vs[32][4];                       // value scales, [row][group]
-    float pp[8][32];                       // softmax weights, [head][token]
-    f16 ap[16][kTokStride];                // p*s of one value group, hi/lo rows
+    float vs[4][32 + 4];                   // value scales, [group][row]
+    float pp[8][32 + 4];                   // softmax weights, [head][token]
+    f16 ap[4][16][kTokStride];             // p*s per value group, hi/lo rows
     f16 apz[16][kTokStride];               // p, hi/lo rows
 };
 
 // Per-wave running softmax state and output accumulators for the two heads
 // this lane's MFMA rows hold (a = 2*kq, b = 2*kq + 1).
+template <int D>
 struct Acc {
     float m_a, m_b, l_a, l_b;
-    f4 o[kMaxD / 16];   // MFMA output tiles of 16 channels
+    f4 o[D / 16];       // MFMA output tiles of 16 channels
     f4 z;               // value zero-point term, columns = value groups
 };
 
 // Online-softmax update with scores x (log2 units) of two 16-token tiles;
 // returns the block weights p in xa/xb and rescales the accumulators.
-__device__ __forceinline__ void softmax_block(Acc& acc, float xa[2], float xb[2], int n_tiles16) {
+template <int D>
+__device__ __forceinline__ void softmax_block(Acc<D>& acc, float xa[2], float xb[2]) {
     const float bm_a = row16_max(fmaxf(xa[0], xa[1]));
     const float bm_b = row16_max(fmaxf(xb[0], xb[1]));
     const float mn_a = fmaxf(acc.m_a, bm_a), mn_b = fmaxf(acc.m_b, bm_b);
@@ -159,14 +173,14 @@ __device__ __forceinline__ void softmax_block(Acc& acc, float xa[2], float xb[2]
     acc.l_b = acc.l_b * al_b + row16_sum(xb[0] + xb[1]);
     acc.m_a = mn_a;
     acc.m_b = mn_b;
+    // once the running maxima settle, alpha is exactly 1 everywhere: skip
+    if (__ballot(al_a != 1.0f || al_b != 1.0f) == 0) return;
 #pragma unroll
-    for (int nt = 0; nt < kMaxD / 16; ++nt) {
-        if (nt < n_tiles16) {
-            acc.o[nt][0] *= al_a;
-            acc.o[nt][1] *= al_a;
-            acc.o[nt][2] *= al_b;
-            acc.o[nt][3] *= al_b;
-        }
+    for (int nt = 0; nt < D / 16; ++nt) {
+        acc.o[nt][0] *= al_a;
+        acc.o[nt][1] *= al_a;
+        acc.o[nt][2] *= al_b;
+        acc.o[nt][3] *= al_b;
     }
     acc.z[0] *= al_a;
     acc.z[1] *= al_a;
@@ -176,16 +190,15 @@ __device__ __forceinline__ void softmax_block(Acc& acc, float xa[2], float xb[2]
 
 // Softmax weights of the block to LDS ([head][token]) and, as hi/lo fp16
 // rows, to the operand apz ([2h / 2h+1][token]).
-template <int KB, int VB>
-__device__ __forceinline__ void weights_to_lds(Smem<KB, VB>& sm, const float pa[2], const float pb[2],
-                                               int r) {
+template <class SM>
+__device__ __forceinline__ void weights_to_lds(SM& sm, const float pa[2], const float pb[2], int r) {
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
         sm.pp[2 * kq][16 * tt + j] = pa[tt];
         sm.pp[2 * kq + 1][16 * tt + j] = pb[tt];
     }
-    __syncthreads();
+    lds_order();
     const int t = L & 31;
     for (int h = L >> 5; h < r; h += 2) {
         f16 hi, lo;
@@ -193,33 +206,29 @@ __device__ __forceinline__ void weights_to_lds(Smem<KB, VB>& sm, const float pa[
         sm.apz[2 * h][t] = hi;
         sm.apz[2 * h + 1][t] = lo;
     }
-    __syncthreads();
+    lds_order();
 }
 
-template <int KB, int VB>
-__device__ __forceinline__ void write_result(const AttnArgs& a, const Acc& acc, int64_t s, int split,
+template <int D>
+__device__ __forceinline__ void write_result(const AttnArgs& a, const Acc<D>& acc, int64_t s, int split,
                                              const float oa[], const float ob[]) {
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
-    const int D = a.head_dim, r = a.q_per_kv, nt16 = D / 16;
+    const int r = a.q_per_kv;
     const int ha = 2 * kq, hb = 2 * kq + 1;
     if (a.plan.n_splits == 1) {
         const float ia = 1.0f / acc.l_a, ib = 1.0f / acc.l_b;
 #pragma unroll
-        for (int nt = 0; nt < kMaxD / 16; ++nt) {
-            if (nt < nt16) {
-                if (ha < r) a.out[(s * r + ha) * D + 16 * nt + j] = __builtin_bit_cast(uint16_t, (f16)(oa[nt] * ia));
-                if (hb < r) a.out[(s * r + hb) * D + 16 * nt + j] = __builtin_bit_cast(uint16_t, (f16)(ob[nt] * ib));
-            }
+        for (int nt = 0; nt < D / 16; ++nt) {
+            if (ha < r) a.out[(s * r + ha) * D + 16 * nt + j] = __builtin_bit_cast(uint16_t, (f16)(oa[nt] * ia));
+            if (hb < r) a.out[(s * r + hb) * D + 16 * nt + j] = __builtin_bit_cast(uint16_t, (f16)(ob[nt] * ib));
         }
         return;
     }
     const int64_t base = (s * a.plan.n_splits + split) * r;
 #pragma unroll
-    for (int nt = 0; nt < kMaxD / 16; ++nt) {
-        if (nt < nt16) {
-            if (ha < r) a.ws_o[(base + ha) * D + 16 * nt + j] = oa[nt];
-            if (hb < r) a.ws_o[(base + hb) * D + 16 * nt + j] = ob[nt];
-        }
+    for (int nt = 0; nt < D / 16; ++nt) {
+        if (ha < r) a.ws_o[(base + ha) * D + 16 * nt + j] = oa[nt];
+        if (hb < r) a.ws_o[(base + hb) * D + 16 * nt + j] = ob[nt];
     }
     if (j == 0) {
         if (ha < r) {
@@ -237,47 +246,45 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Acc& acc, 
 // the attention kernel: blockIdx.x = slice * n_splits + split
 // ---------------------------------------------------------------------------
 
-template <int KB, int VB>
+template <int KB, int VB, int D>
 __global__ void __launch_bounds__(kWave) attention_kernel(const AttnArgs a) {
-    __shared__ Smem<KB, VB> sm;
+    constexpr int NK32 = D / 32, NT16 = D / 16;
+    __shared__ Smem<KB, VB, D> sm;
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
-    const int D = a.head_dim, G = a.group_size, r = a.q_per_kv;
-    const int nk32 = D / 32, nt16 = D / 16;
+    const int G = a.group_size, r = a.q_per_kv;
     const int64_t s = blockIdx.x / a.plan.n_splits;
     const int split = (int)(blockIdx.x - s * a.plan.n_splits);
     const bool residual = a.plan.has_res && split == a.plan.n_splits - 1;
 
     // operand rows that are never written stay zero
-    for (int i = L; i < 16 * kAqStride; i += kWave) (&sm.aq[0][0])[i] = (f16)0;
-    for (int i = L; i < 16 * kTokStride; i += kWave) {
-        (&sm.ap[0][0])[i] = (f16)0;
-        (&sm.apz[0][0])[i] = (f16)0;
+    for (int i = L; i < 16 * (D + 8); i += kWave) (&sm.aq[0][0])[i] = (f16)0;
+    for (int i = L; i < 4 * 16 * kTokStride; i += kWave) (&sm.ap[0][0][0])[i] = (f16)0;
+    for (int i = L; i < 16 * kTokStride; i += kWave) (&sm.apz[0][0])[i] = (f16)0;
+    // the queries to LDS; rows of heads >= r are zero
+    for (int i = L; i < D; i += kWave) {
+        const int h = i / (D / 8), c = 8 * (i - h * (D / 8));
+        u32x4 w = u32x4{0, 0, 0, 0};
+        if (h < r) w = *reinterpret_cast<const u32x4*>(a.q + (s * r + h) * D + c);
+        *reinterpret_cast<u32x4*>(&sm.q[h][c]) = w;
     }
-
     // q as MFMA A operand, rows 2h = q_h and 2h+1 = 0: lane row j, channels
-    // 32*kk + 8*kq .. +7
-    h8 qa[kMaxD / 32];
-    {
-        const int h = j >> 1;
-        const bool live = (j & 1) == 0 && h < r;
-        const uint16_t* qrow = a.q + (s * r + (live ? h : 0)) * D;
-#pragma unroll
-        for (int kk = 0; kk < kMaxD / 32; ++kk) {
-            u32x4 w = u32x4{0, 0, 0, 0};
-            if (live && kk < nk32) w = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * kq);
-            qa[kk] = __builtin_bit_cast(h8, w);
-        }
-    }
+    // 32*kk + 8*kq .. +7 (odd rows read a zero row of aq's initial state is not
+    // guaranteed, so they are masked)
+    const bool qrow_live = (j & 1) == 0;
+    auto qa = [&](int kk) {
+        const h8 v = lds_h8(&sm.q[j >> 1][32 * kk + 8 * kq]);
+        return qrow_live ? v : __builtin_bit_cast(h8, u32x4{0, 0, 0, 0});
+    };
 
-    Acc acc;
+    Acc<D> acc;
     acc.m_a = acc.m_b = kNegInf;
     acc.l_a = acc.l_b = 0.0f;
 #pragma unroll
-    for (int nt = 0; nt < kMaxD / 16; ++nt) acc.o[nt] = f4{0, 0, 0, 0};
+    for (int nt = 0; nt < NT16; ++nt) acc.o[nt] = f4{0, 0, 0, 0};
     acc.z = f4{0, 0, 0, 0};
     __syncthreads();
 
-    float oa[kMaxD / 16], ob[kMaxD / 16];
+    float oa[NT16], ob[NT16];
 
     if (residual) {
         // ---- fp16 residual: plain fp16 operands ----
@@ -292,23 +299,23 @@ __global__ void __launch_bounds__(kWave) attention_kernel(const AttnArgs a) {
                 int slot = a.res_head + (valid ? i : 0);
                 if (slot >= a.res_slots) slot -= a.res_slots;
                 const uint16_t* row = rk + (int64_t)slot * D;
+                u32x4 w[NK32];
+#pragma unroll
+                for (int kk = 0; kk < NK32; ++kk) {
+                    w[kk] = *reinterpret_cast<const u32x4*>(row + 32 * kk + 8 * kq);
+                    if (!valid) w[kk] = u32x4{0, 0, 0, 0};
+                }
                 f4 sc = f4{0, 0, 0, 0};
 #pragma unroll
-                for (int kk = 0; kk < kMaxD / 32; ++kk) {
-                    if (kk < nk32) {
-                        u32x4 w = u32x4{0, 0, 0, 0};
-                        if (valid) w = *reinterpret_cast<const u32x4*>(row + 32 * kk + 8 * kq);
-                        sc = mfma(qa[kk], __builtin_bit_cast(h8, w), sc);
-                    }
-                }
+                for (int kk = 0; kk < NK32; ++kk) sc = mfma(qa(kk), __builtin_bit_cast(h8, w[kk]), sc);
                 xa[tt] = valid ? (sc[0] + sc[1]) * a.logit_scale : kNegInf;
                 xb[tt] = valid ? (sc[2] + sc[3]) * a.logit_scale : kNegInf;
             }
-            softmax_block(acc, xa, xb, nt16);
+            softmax_block(acc, xa, xb);
             weights_to_lds(sm, xa, xb, r);
             // values: B[token 8kq+e][channel 16nt+j]
-            const h8 pa8 = *reinterpret_cast<const h8*>(&sm.apz[j][8 * kq]);
-            int slots[8];
+            const h8 pa8 = lds_h8(&sm.apz[j][8 * kq]);
+            const uint16_t* vrow[8];
             bool valid[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -316,28 +323,26 @@ __global__ void __launch_bounds__(kWave) attention_kernel(const AttnArgs a) {
                 valid[e] = i < a.res_count;
                 int slot = a.res_head + (valid[e] ? i : 0);
                 if (slot >= a.res_slots) slot -= a.res_slots;
-                slots[e] = slot;
+                vrow[e] = rv + (int64_t)slot * D + j;
             }
 #pragma unroll
-            for (int nt = 0; nt < kMaxD / 16; ++nt) {
-                if (nt < nt16) {
-                    h8 b;
+            for (int nt = 0; nt < NT16; ++nt) {
+                h8 b;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint16_t x = valid[e] ? rv[(int64_t)slots[e] * D + 16 * nt + j] : (uint16_t)0;
-                        b[e] = __builtin_bit_cast(f16, x);
-                    }
-                    acc.o[nt] = mfma(pa8, b, acc.o[nt]);
+                for (int e = 0; e < 8; ++e) {
+                    const uint16_t x = vrow[e][16 * nt];
+                    b[e] = __builtin_bit_cast(f16, valid[e] ? x : (uint16_t)0);
                 }
+                acc.o[nt] = mfma(pa8, b, acc.o[nt]);
             }
-            __syncthreads();   // pp / apz are rewritten by the next block
+            lds_order();       // pp / apz are rewritten by the next block
         }
 #pragma unroll
-        for (int nt = 0; nt < kMaxD / 16; ++nt) {
+        for (int nt = 0; nt < NT16; ++nt) {
             oa[nt] = acc.o[nt][0] + acc.o[nt][1];
             ob[nt] = acc.o[nt][2] + acc.o[nt][3];
         }
-        write_result<KB, VB>(a, acc, s, split, oa, ob);
+        write_result<D>(a, acc, s, split, oa, ob);
         return;
     }
 
@@ -349,112 +354,140 @@ __global__ void __launch_bounds__(kWave) attention_kernel(const AttnArgs a) {
     const int ngk_cap = (a.cap_tokens + G - 1) / G;
     const int ngv = (D + G - 1) / G;
     const int wpt = ngv * G * VB / 32;                    // value words per row
-    const int vcols = D * VB / 32;                        // value words that hold real channels
+    constexpr int VPAIRS = D * VB / 64;                   // word pairs per row that hold real channels
     const uint32_t* kcs = a.k_codes + s * (int64_t)ngk_cap * Wk * D;
     const uint16_t* kss = a.k_scale + s * (int64_t)ngk_cap * D;
     const uint16_t* kzs = a.k_zero + s * (int64_t)ngk_cap * D;
     const uint32_t* vcs = a.v_codes + s * (int64_t)a.cap_tokens * wpt;
     const uint16_t* vss = a.v_scale + s * (int64_t)a.cap_tokens * ngv;
     const uint16_t* vzs = a.v_zero + s * (int64_t)a.cap_tokens * ngv;
+    const bool pair_live = 2 * L < D;                     // this lane's channel pair (2L, 2L+1) exists
 
-    // q of channel pair (2L, 2L+1) for the q*s operand
-    float qf[8][2];
-    const bool pair_live = 2 * L < D;
+    // One block's global data, held in registers from the previous block's
+    // compute until it is written to LDS (so its load latency is hidden).
+    constexpr int KCH = KB * D / 4;                       // 16-byte key-code chunks per block
+    constexpr int KV = (KCH + kWave - 1) / kWave;
+    constexpr int VV = (32 * VPAIRS + kWave - 1) / kWave; // value-code word pairs per lane
+    struct Stage {
+        u32x4 k[KV];
+        uint32_t v[VV][2];
+        uint16_t vsb[2], vzb[2];
+        uint32_t ks, kz;
+    };
+    auto load = [&](int blk, Stage& st) {
+        const int t0 = 32 * blk, g = t0 / G;
+        const uint32_t* srck = kcs + ((int64_t)g * Wk + ((t0 % G) / 32) * KB) * D;
 #pragma unroll
-    for (int h = 0; h < 8; ++h) {
-        qf[h][0] = qf[h][1] = 0.0f;
-        if (h < r && pair_live) {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(a.q + (s * r + h) * D + 2 * L);
-            qf[h][0] = (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xFFFF));
-            qf[h][1] = (float)__builtin_bit_cast(f16, (uint16_t)(w >> 16));
+        for (int i = 0; i < KV; ++i) {
+            const int v = L + kWave * i;
+            if (v < KCH) st.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(srck) + v);
         }
-    }
+#pragma unroll
+        for (int i = 0; i < VV; ++i) {
+            const int e = L + kWave * i;
+            st.v[i][0] = st.v[i][1] = 0;
+            if (e < 32 * VPAIRS) {
+                const int row = e / VPAIRS, c2 = 2 * (e - row * VPAIRS);
+                if (t0 + row < n) {
+                    const uint32_t* src = vcs + (int64_t)(t0 + row) * wpt + c2;
+                    st.v[i][0] = __builtin_nontemporal_load(src);
+                    st.v[i][1] = __builtin_nontemporal_load(src + 1);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = L + kWave * i;
+            st.vsb[i] = st.vzb[i] = 0;
+            if (e < 32 * ngv) {
+                const int row = e / ngv, gv = e - row * ngv;
+                if (t0 + row < n) {
+                    st.vsb[i] = vss[(int64_t)(t0 + row) * ngv + gv];
+                    st.vzb[i] = vzs[(int64_t)(t0 + row) * ngv + gv];
+                }
+            }
+        }
+        if ((t0 % G == 0 || blk == b0) && pair_live) {
+            st.ks = *reinterpret_cast<const uint32_t*>(kss + (int64_t)g * D + 2 * L);
+            st.kz = *reinterpret_cast<const uint32_t*>(kzs + (int64_t)g * D + 2 * L);
+        }
+    };
+    auto commit = [&](int blk, const Stage& st) {
+        const int t0 = 32 * blk;
+#pragma unroll
+        for (int i = 0; i < KV; ++i) {
+            const int v = L + kWave * i;
+            if (v < KCH) {
+                const int row = (4 * v) / D, col = (4 * v) % D;
+                *reinterpret_cast<u32x4*>(&sm.kc[row][col]) = st.k[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VV; ++i) {
+            const int e = L + kWave * i;
+            if (e < 32 * VPAIRS) {
+                const int row = e / VPAIRS, c2 = 2 * (e - row * VPAIRS);
+                sm.vc[c2][row] = st.v[i][0];
+                sm.vc[c2 + 1][row] = st.v[i][1];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int e = L + kWave * i;
+            if (e < 32 * ngv) {
+                const int row = e / ngv, gv = e - row * ngv;
+                sm.vs[gv][row] = (float)__builtin_bit_cast(f16, st.vsb[i]);
+                sm.vz[gv][row] = __builtin_bit_cast(f16, st.vzb[i]);
+            }
+        }
+        // a new key group: q*s operand rows (fp32 product split hi/lo) and zeros
+        if ((t0 % G == 0 || blk == b0) && pair_live) {
+            const float s0 = (float)__builtin_bit_cast(f16, (uint16_t)(st.ks & 0xFFFF));
+            const float s1 = (float)__builtin_bit_cast(f16, (uint16_t)(st.ks >> 16));
+            *reinterpret_cast<uint32_t*>(&sm.kz[2 * L]) = st.kz;
+            for (int h = 0; h < r; ++h) {
+                const uint32_t qw = *reinterpret_cast<const uint32_t*>(&sm.q[h][2 * L]);
+                const float q0 = (float)__builtin_bit_cast(f16, (uint16_t)(qw & 0xFFFF));
+                const float q1 = (float)__builtin_bit_cast(f16, (uint16_t)(qw >> 16));
+                f16 h0, l0, h1, l1;
+                split_hl(q0 * s0, h0, l0);
+                split_hl(q1 * s1, h1, l1);
+                *reinterpret_cast<uint32_t*>(&sm.aq[2 * h][2 * L]) = pack_h2(h0, h1);
+                *reinterpret_cast<uint32_t*>(&sm.aq[2 * h + 1][2 * L]) = pack_h2(l0, l1);
+            }
+        }
+    };
 
     const CodePos<KB> kpos(j % (32 / KB));
     const CodePos<VB> vpos(j % (32 / VB));
     f4 zk = f4{0, 0, 0, 0};
-    int cur_group = -1;
+    Stage stage;
+    if (b0 < b1) load(b0, stage);
 
     for (int blk = b0; blk < b1; ++blk) {
         const int t0 = 32 * blk;
-        const int g = t0 / G;
-        // key statistics of a new group: q*s operand rows and zeros
-        if (g != cur_group) {
-            cur_group = g;
-            if (pair_live) {
-                const uint32_t sw = *reinterpret_cast<const uint32_t*>(kss + (int64_t)g * D + 2 * L);
-                const uint32_t zw = *reinterpret_cast<const uint32_t*>(kzs + (int64_t)g * D + 2 * L);
-                const float s0 = (float)__builtin_bit_cast(f16, (uint16_t)(sw & 0xFFFF));
-                const float s1 = (float)__builtin_bit_cast(f16, (uint16_t)(sw >> 16));
-                *reinterpret_cast<uint32_t*>(&sm.kz[2 * L]) = zw;
-#pragma unroll
-                for (int h = 0; h < 8; ++h) {
-                    if (h < r) {
-                        f16 h0, l0, h1, l1;
-                        split_hl(qf[h][0] * s0, h0, l0);
-                        split_hl(qf[h][1] * s1, h1, l1);
-                        *reinterpret_cast<uint32_t*>(&sm.aq[2 * h][2 * L]) = pack_h2(h0, h1);
-                        *reinterpret_cast<uint32_t*>(&sm.aq[2 * h + 1][2 * L]) = pack_h2(l0, l1);
-                    }
-                }
-            }
-        }
-        // stage the block: key codes (KB word rows of D words, contiguous)
-        {
-            const uint32_t* src = kcs + ((int64_t)g * Wk + ((t0 % G) / 32) * KB) * D;
-            for (int v = L; v < KB * D / 4; v += kWave) {
-                const int row = (4 * v) / D, col = (4 * v) % D;
-                *reinterpret_cast<u32x4*>(&sm.kc[row][col]) = *reinterpret_cast<const u32x4*>(src + 4 * v);
-            }
-        }
-        // value codes of rows t0 .. t0+31 (word columns < vcols), transposed;
-        // rows past n_quant are zero (and never read from memory)
-        for (int v = L; v < 32 * (vcols / 2); v += kWave) {
-            const int row = v / (vcols / 2), c2 = 2 * (v % (vcols / 2));
-            const int t = t0 + row;
-            uint32_t w0 = 0, w1 = 0;
-            if (t < n) {
-                const uint32_t* src = vcs + (int64_t)t * wpt + c2;
-                w0 = src[0];
-                w1 = src[1];
-            }
-            sm.vc[c2][row] = w0;
-            sm.vc[c2 + 1][row] = w1;
-        }
-        // value statistics of the 32 rows
-        for (int v = L; v < 32 * ngv; v += kWave) {
-            const int row = v / ngv, gv = v % ngv;
-            const int t = t0 + row;
-            uint16_t sb = 0, zb = 0;
-            if (t < n) {
-                sb = vss[(int64_t)t * ngv + gv];
-                zb = vzs[(int64_t)t * ngv + gv];
-            }
-            sm.vs[row][gv] = (float)__builtin_bit_cast(f16, sb);
-            sm.vz[gv][row] = __builtin_bit_cast(f16, zb);
-        }
-        __syncthreads();
+        commit(blk, stage);
+        lds_order();
+        if (blk + 1 < b1) load(blk + 1, stage);
 
-        // keys: scores of two 16-token tiles, and the zero-point term
+        // keys: the zero-point term of a new group, then the scores of two
+        // 16-token tiles
         if (t0 % G == 0 || blk == b0) {
             zk = f4{0, 0, 0, 0};
 #pragma unroll
-            for (int kk = 0; kk < kMaxD / 32; ++kk)
-                if (kk < nk32) zk = mfma(qa[kk], *reinterpret_cast<const h8*>(&sm.kz[32 * kk + 8 * kq]), zk);
+            for (int kk = 0; kk < NK32; ++kk) zk = mfma(qa(kk), lds_h8(&sm.kz[32 * kk + 8 * kq]), zk);
         }
         f4 sc[2] = {f4{0, 0, 0, 0}, f4{0, 0, 0, 0}};
 #pragma unroll
-        for (int kk = 0; kk < kMaxD / 32; ++kk) {
-            if (kk < nk32) {
-                const h8 aop = *reinterpret_cast<const h8*>(&sm.aq[j][32 * kk + 8 * kq]);
+        for (int kk = 0; kk < NK32; ++kk) {
+            const h8 aop = lds_h8(&sm.aq[j][32 * kk + 8 * kq]);
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const int wi = (16 * tt + j) / (32 / KB);
-                    const uint32_t* wp = &sm.kc[wi][32 * kk + 8 * kq];
-                    const h8 bop = codes8<KB>(*reinterpret_cast<const u32x4*>(wp),
-                                              *reinterpret_cast<const u32x4*>(wp + 4), kpos);
-                    sc[tt] = mfma(aop, bop, sc[tt]);
-                }
+            for (int tt = 0; tt < 2; ++tt) {
+                const int wi = (16 * tt + j) / (32 / KB);
+                const uint32_t* wp = &sm.kc[wi][32 * kk + 8 * kq];
+                const h8 bop = codes8<KB>(*reinterpret_cast<const u32x4*>(wp),
+                                          *reinterpret_cast<const u32x4*>(wp + 4), kpos);
+                sc[tt] = mfma(aop, bop, sc[tt]);
             }
         }
         float xa[2], xb[2];
@@ -464,58 +497,54 @@ __global__ void __launch_bounds__(kWave) attention_kernel(const AttnArgs a) {
             xa[tt] = valid ? ((sc[tt][0] + sc[tt][1]) * kpos.col + zk[0]) * a.logit_scale : kNegInf;
             xb[tt] = valid ? ((sc[tt][2] + sc[tt][3]) * kpos.col + zk[2]) * a.logit_scale : kNegInf;
         }
-        softmax_block(acc, xa, xb, nt16);
+        softmax_block(acc, xa, xb);
         weights_to_lds(sm, xa, xb, r);
 
-        // values: zero-point term over all groups at once (columns = groups)
+        // values: the p*s operand of every value group
         {
-            const h8 pz = *reinterpret_cast<const h8*>(&sm.apz[j][8 * kq]);
-            h8 bz = __builtin_bit_cast(h8, u32x4{0, 0, 0, 0});
-            if (j < ngv) bz = *reinterpret_cast<const h8*>(&sm.vz[j][8 * kq]);
-            acc.z = mfma(pz, bz, acc.z);
-        }
-        // values: p*s operand per value group, then the code tiles of that group
-        int cur_vg = -1;
-        const int t = L & 31;
-#pragma unroll
-        for (int nt = 0; nt < kMaxD / 16; ++nt) {
-            if (nt < nt16) {
-                const int gv = (16 * nt) / G;
-                if (gv != cur_vg) {
-                    cur_vg = gv;
-                    if (nt > 0) __syncthreads();
-                    const float sv = sm.vs[t][gv];
-                    for (int h = L >> 5; h < r; h += 2) {
-                        f16 hi, lo;
-                        split_hl(sm.pp[h][t] * sv, hi, lo);
-                        sm.ap[2 * h][t] = hi;
-                        sm.ap[2 * h + 1][t] = lo;
-                    }
-                    __syncthreads();
+            const int t = L & 31;
+            for (int h = L >> 5; h < r; h += 2) {
+                const float p = sm.pp[h][t];
+                for (int gv = 0; gv < ngv; ++gv) {
+                    f16 hi, lo;
+                    split_hl(p * sm.vs[gv][t], hi, lo);
+                    sm.ap[gv][2 * h][t] = hi;
+                    sm.ap[gv][2 * h + 1][t] = lo;
                 }
-                const h8 aop = *reinterpret_cast<const h8*>(&sm.ap[j][8 * kq]);
-                const int col = (16 * nt + j) / (32 / VB);
-                const uint32_t* wp = &sm.vc[col][8 * kq];
-                const h8 bop = codes8<VB>(*reinterpret_cast<const u32x4*>(wp),
-                                          *reinterpret_cast<const u32x4*>(wp + 4), vpos);
-                acc.o[nt] = mfma(aop, bop, acc.o[nt]);
             }
         }
-        __syncthreads();   // the staging buffers are rewritten by the next block
+        lds_order();
+        // values: zero-point term over all groups at once (columns = groups)
+        {
+            const h8 pz = lds_h8(&sm.apz[j][8 * kq]);
+            const h8 bz = lds_h8(&sm.vz[j < ngv ? j : 0][8 * kq]);
+            acc.z = mfma(pz, j < ngv ? bz : __builtin_bit_cast(h8, u32x4{0, 0, 0, 0}), acc.z);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT16; ++nt) {
+            const int gv = (16 * nt) / G;
+            const h8 aop = lds_h8(&sm.ap[gv][j][8 * kq]);
+            const int col = (16 * nt + j) / (32 / VB);
+            const uint32_t* wp = &sm.vc[col][8 * kq];
+            const h8 bop = codes8<VB>(*reinterpret_cast<const u32x4*>(wp),
+                                      *reinterpret_cast<const u32x4*>(wp + 4), vpos);
+            acc.o[nt] = mfma(aop, bop, acc.o[nt]);
+        }
+        lds_order();   // the next block's commit overwrites what this one read
     }
 
     // output = code term * column factor + zero term of the channel's group;
     // the zero term of group gv sits in column gv of the same 16-lane row
     const float za = acc.z[0] + acc.z[1], zb = acc.z[2] + acc.z[3];
 #pragma unroll
-    for (int nt = 0; nt < kMaxD / 16; ++nt) {
+    for (int nt = 0; nt < NT16; ++nt) {
         const int gv = (16 * nt) / G;
         const float zra = __shfl(za, 16 * kq + gv, kWave);
         const float zrb = __shfl(zb, 16 * kq + gv, kWave);
         oa[nt] = (acc.o[nt][0] + acc.o[nt][1]) * vpos.col + zra;
         ob[nt] = (acc.o[nt][2] + acc.o[nt][3]) * vpos.col + zrb;
     }
-    write_result<KB, VB>(a, acc, s, split, oa, ob);
+    write_result<D>(a, acc, s, split, oa, ob);
 }
 
 // Merge of the partial results of a split slice: one workgroup per (slice,
@@ -541,10 +570,10 @@ __global__ void __launch_bounds__(kWave) attention_merge_kernel(const AttnArgs a
     if (L + kWave < D) dst[L + kWave] = __builtin_bit_cast(uint16_t, (f16)(o1 * inv));
 }
 
-template <int KB, int VB>
+template <int KB, int VB, int D>
 int run_attention(const AttnArgs& a, hipStream_t st) {
     const int64_t groups = a.n_slices * a.plan.n_splits;
-    hipLaunchKernelGGL((attention_kernel<KB, VB>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
+    hipLaunchKernelGGL((attention_kernel<KB, VB, D>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (a.plan.n_splits > 1) {
@@ -560,8 +589,16 @@ int run_attention(const AttnArgs& a, hipStream_t st) {
 int launch_attention(const AttnArgs& a, void* stream) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (a.n_slices == 0) return 0;
-#define KIVI_ATTN(KB, VB) \
-    if (a.k_bits == KB && a.v_bits == VB) return run_attention<KB, VB>(a, st);
+#define KIVI_ATTN(KB, VB)                                                              \
+    if (a.k_bits == KB && a.v_bits == VB) {                                            \
+        switch (a.head_dim) {                                                          \
+            case 32: return run_attention<KB, VB, 32>(a, st);                          \
+            case 64: return run_attention<KB, VB, 64>(a, st);                          \
+            case 96: return run_attention<KB, VB, 96>(a, st);                          \
+            case 128: return run_attention<KB, VB, 128>(a, st);                        \
+            default: return (int)hipErrorInvalidValue;                                 \
+        }                                                                              \
+    }
     KIVI_ATTN(2, 2) KIVI_ATTN(2, 4) KIVI_ATTN(2, 8)
     KIVI_ATTN(4, 2) KIVI_ATTN(4, 4) KIVI_ATTN(4, 8)
     KIVI_ATTN(8, 2) KIVI_ATTN(8, 4) KIVI_ATTN(8, 8)

@@ -9,6 +9,7 @@ arithmetic and imports neither the codec nor the oracle.
 from .workloads import (  # noqa: F401
     WORKLOADS,
     Workload,
+    decode_queries,
     layer_kv,
     stream_tokens,
     uniform_with_ties,

@@ -39,6 +39,7 @@ class Workload:
     group_size: int
     residual_length: int
     steps: int = 0          # streaming decode steps (0 = full-cache encode)
+    q_per_kv: int = 1       # query heads per KV head at decode (grouped-query attention)
 
     @property
     def slices_per_layer(self) -> int:
@@ -55,7 +56,7 @@ WORKLOADS = {
     "llama2_7b_2bit": Workload(2, "Llama-2-7B-shaped cache, batch 8, 4096 tokens, 2/2-bit",
                                32, 8, 32, 4096, 128, 2, 2, 32, 128),
     "mistral_7b_k2v4": Workload(3, "Mistral-7B-shaped GQA cache, batch 16, 16384 tokens, K2/V4",
-                                32, 16, 8, 16384, 128, 2, 4, 32, 128),
+                                32, 16, 8, 16384, 128, 2, 4, 32, 128, q_per_kv=4),
     "stream_b64": Workload(4, "streaming decode, batch 64, prefill 2048 + 512 steps, 2/2-bit",
                            32, 64, 8, 2048, 128, 2, 2, 32, 128, steps=512),
 }
@@ -129,6 +130,13 @@ def layer_kv(w: Workload, layer: int, device="cpu", tokens: int | None = None):
     k = k.to(torch.float16).reshape(w.batch * w.heads, T, D)
     v = v.to(torch.float16).reshape(w.batch * w.heads, T, D)
     return k, v
+
+
+def decode_queries(w: Workload, device="cpu"):
+    """One decode step's query vectors for every slice: fp16
+    ``[L*B*H, q_per_kv, D]``, N(0,1) (seed ``1000*c + 950``)."""
+    g = _gen(device, 1000 * w.number + 950)
+    return _normal((w.slices, w.q_per_kv, w.head_dim), g, device).to(torch.float16)
 
 
 def stream_tokens(w: Workload, steps: int, device="cpu"):
