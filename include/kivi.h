@@ -225,6 +225,46 @@ int kivi_stream_prefill(const kivi_config* cfg, kivi_stream* st,
 int kivi_append_flush(const kivi_config* cfg, kivi_stream* st,
                       const void* k_new_fp16, const void* v_new_fp16, void* hip_stream);
 
+/* Compact host image of a streaming cache (CacheSeek PR #4 "Feature
+ * (quantization): add KIVI KV-cache quantization for exact-prefix reuse":
+ * encoding runs on the source device, only the compact qdata/scale/offset
+ * payload travels to host memory for storage, and decoding moves only that
+ * payload to the target device before dequantizing).  The image holds, for
+ * every slice, the quantized prefix of n_quant tokens and the fp16 residual
+ * ring, as eight arrays one after another, each slice-major and packed
+ * without the device arrays' unused capacity:
+ *   key codes   [n_slices][NG_k(n_quant)*W_k][D]  int32
+ *   key scale   [n_slices][NG_k(n_quant)][D]      fp16   (then key zero)
+ *   value codes [n_slices][n_quant][NG_v*W_v]     int32
+ *   value scale [n_slices][n_quant][NG_v]         fp16   (then value zero)
+ *   key ring    [n_slices][R + G][D]              fp16   (then value ring)
+ * Ring slots are copied as they are, so the image keeps ring_head and
+ * ring_count meaningful; the caller stores those counters with it.
+ * kivi_stream_image_bytes returns the image size (-1 on invalid input);
+ * n_quant must be a multiple of G, as in every kivi_stream. */
+int64_t kivi_stream_image_bytes(const kivi_config* cfg, int64_t n_slices, int64_t n_quant);
+
+/* Enqueues the copies of st's image (at st->n_quant tokens) into host
+ * memory `host` (host_bytes >= the image size; pinned memory makes the
+ * copies asynchronous).  Device arrays and counters are not modified.
+ * KIVI_E_SHAPE when host_bytes is too small, KIVI_E_STATE for inconsistent
+ * counters. */
+int kivi_stream_offload(const kivi_config* cfg, const kivi_stream* st, void* host,
+                        int64_t host_bytes, void* hip_stream);
+
+/* Enqueues the copies of an image of n_quant tokens from host memory into
+ * st's device arrays (st->n_slices slices, capacity st->cap_tokens >=
+ * n_quant) and sets st->n_quant, ring_head and ring_count to the given
+ * values, which must satisfy the kivi_stream invariants (KIVI_E_STATE
+ * otherwise; KIVI_E_CAPACITY when n_quant > cap_tokens).  The value rows
+ * of the residual tokens (rows n_quant .. n_quant + ring_count - 1 below
+ * capacity, which a kivi_stream quantizes on arrival) are not part of the
+ * image: the restore re-quantizes them from the restored ring, so the
+ * stream continues exactly as the one that was offloaded. */
+int kivi_stream_restore(const kivi_config* cfg, kivi_stream* st, const void* host,
+                        int64_t host_bytes, int64_t n_quant, int64_t ring_head,
+                        int64_t ring_count, void* hip_stream);
+
 /* Decode-phase attention over the quantized cache (CacheForge README,
  * "Contribution scope": the inherited KIVI code brings the model
  * integrations and the kernels that consume the quantized cache; "How it

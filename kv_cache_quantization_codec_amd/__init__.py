@@ -22,7 +22,10 @@ from .binding import (  # noqa: E402,F401
     kivi_k_code_words,
     kivi_k_stat_elems,
     kivi_ring_elems,
+    kivi_stream_image_bytes,
+    kivi_stream_offload,
     kivi_stream_prefill,
+    kivi_stream_restore,
     kivi_v_code_words,
     kivi_v_stat_elems,
 )

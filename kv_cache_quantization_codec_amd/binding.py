@@ -78,6 +78,9 @@ SIGNATURES = [
     ("kivi_decode_v", _I32, [_CFG, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     ("kivi_stream_prefill", _I32, [_CFG, _ST, _P, _P, _I64, _I64, _P]),
     ("kivi_append_flush", _I32, [_CFG, _ST, _P, _P, _P]),
+    ("kivi_stream_image_bytes", _I64, [_CFG, _I64, _I64]),
+    ("kivi_stream_offload", _I32, [_CFG, _ST, _P, _I64, _P]),
+    ("kivi_stream_restore", _I32, [_CFG, _ST, _P, _I64, _I64, _I64, _I64, _P]),
     ("kivi_attention_workspace_bytes", _I64, [_CFG, _I64, _I32, _I64, _I64]),
     ("kivi_decode_attention", _I32, [_CFG, _AC, _I64, _I32, _P, ctypes.c_float, _P, _P, _I64, _P]),
 ]
@@ -289,6 +292,35 @@ def kivi_append_flush(st: Stream, k_new: torch.Tensor, v_new: torch.Tensor, stre
     _check(lib().kivi_append_flush(_cfg(st.cfg), ctypes.byref(st.state), _ptr(k_new), _ptr(v_new),
                                    _stream_ptr(stream)), "kivi_append_flush")
     return st.state.n_quant != before
+
+
+# ---------------------------------------------------------------------------
+# compact host image of a streaming cache
+# ---------------------------------------------------------------------------
+
+def kivi_stream_image_bytes(cfg, n_slices: int, n_quant: int) -> int:
+    return lib().kivi_stream_image_bytes(_cfg(cfg), n_slices, n_quant)
+
+
+def _host_bytes(host: torch.Tensor) -> int:
+    if host.device.type != "cpu" or not host.is_contiguous():
+        raise ValueError("host image must be a contiguous CPU tensor (pinned for async copies)")
+    return host.numel() * host.element_size()
+
+
+def kivi_stream_offload(st: Stream, host: torch.Tensor, stream=None):
+    """Enqueue the copies of ``st``'s image into ``host`` (uint8 CPU tensor of
+    at least :func:`kivi_stream_image_bytes` bytes)."""
+    _check(lib().kivi_stream_offload(_cfg(st.cfg), ctypes.byref(st.state), _ptr(host), _host_bytes(host),
+                                     _stream_ptr(stream)), "kivi_stream_offload")
+
+
+def kivi_stream_restore(st: Stream, host: torch.Tensor, n_quant: int, ring_head: int, ring_count: int,
+                        stream=None):
+    """Enqueue the copies of an image into ``st`` and set its counters."""
+    _check(lib().kivi_stream_restore(_cfg(st.cfg), ctypes.byref(st.state), _ptr(host), _host_bytes(host),
+                                     n_quant, ring_head, ring_count, _stream_ptr(stream)),
+           "kivi_stream_restore")
 
 
 # ---------------------------------------------------------------------------

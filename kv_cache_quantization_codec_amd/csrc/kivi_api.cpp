@@ -160,6 +160,39 @@ bool flush_due(int64_t count, int64_t residual, int64_t group) {
     return count > residual && count >= group;
 }
 
+// The compact image of a streaming cache: eight arrays, each with the
+// used prefix of every slice packed back to back.  `dev_pitch` is a slice's
+// size in the device arrays (capacity cap), `width` the bytes of n_quant
+// tokens per slice; rings are copied whole (height 1).
+struct ImagePart {
+    int64_t width;
+    int64_t dev_pitch;
+    int64_t height;
+};
+
+bool image_parts(const kivi_config* c, int64_t n_slices, int64_t n_quant, int64_t cap,
+                 ImagePart parts[8], int64_t* total) {
+    const int64_t ring = (int64_t(c->residual_length) + c->group_size) * c->head_dim * 2;
+    const int64_t kcw = k_words(c, n_quant) * 4, kcp = k_words(c, cap) * 4;
+    const int64_t ksw = k_stats(c, n_quant) * 2, ksp = k_stats(c, cap) * 2;
+    const int64_t vcw = v_words(c, n_quant) * 4, vcp = v_words(c, cap) * 4;
+    const int64_t vsw = v_stats(c, n_quant) * 2, vsp = v_stats(c, cap) * 2;
+    int64_t ring_all = 0;
+    if (!mul_ok(n_slices, ring, &ring_all)) return false;
+    const ImagePart p[8] = {{kcw, kcp, n_slices}, {ksw, ksp, n_slices}, {ksw, ksp, n_slices},
+                            {vcw, vcp, n_slices}, {vsw, vsp, n_slices}, {vsw, vsp, n_slices},
+                            {ring_all, ring_all, 1},  {ring_all, ring_all, 1}};
+    int64_t sum = 0;
+    for (int i = 0; i < 8; ++i) {
+        int64_t bytes = 0;
+        if (!mul_ok(p[i].width, p[i].height, &bytes) || __builtin_add_overflow(sum, bytes, &sum))
+            return false;
+        parts[i] = p[i];
+    }
+    *total = sum;
+    return true;
+}
+
 // Decode attention: configuration limits of the attention kernels and the
 // workspace they need (partial softmax sums when a slice is split).
 int check_attention_config(const kivi_config* c, int32_t q_per_kv) {
@@ -425,6 +458,97 @@ int kivi_decode_attention(const kivi_config* cfg, const kivi_attn_cache* cache, 
     a.logit_scale = sm_scale * 1.4426950408889634f;
     a.plan = plan;
     return record(kivi::launch_attention(a, stream));
+}
+
+int64_t kivi_stream_image_bytes(const kivi_config* cfg, int64_t n_slices, int64_t n_quant) {
+    if (check_config(cfg)) return -1;
+    if (n_slices < 0 || n_quant < 0 || n_quant > kMaxTokens || n_quant % cfg->group_size != 0) return -1;
+    ImagePart parts[8];
+    int64_t total = 0;
+    if (!image_parts(cfg, n_slices, n_quant, n_quant, parts, &total)) return -1;
+    return total;
+}
+
+int kivi_stream_offload(const kivi_config* cfg, const kivi_stream* st, void* host, int64_t host_bytes,
+                        void* stream) {
+    int s = check_config(cfg);
+    if (s) return s;
+    s = check_stream(cfg, st, true);
+    if (s) return s;
+    if (st->n_slices == 0) return KIVI_OK;
+    ImagePart parts[8];
+    int64_t total = 0;
+    if (!image_parts(cfg, st->n_slices, st->n_quant, st->cap_tokens, parts, &total)) return KIVI_E_SHAPE;
+    if (host_bytes < total) return KIVI_E_SHAPE;
+    if (!host) return KIVI_E_NULL;
+    const void* src[8] = {st->k_codes, st->k_scale, st->k_zero, st->v_codes,
+                          st->v_scale, st->v_zero,  st->k_ring, st->v_ring};
+    char* dst = static_cast<char*>(host);
+    for (int i = 0; i < 8; ++i) {
+        s = record(kivi::launch_copy_2d(dst, parts[i].width, src[i], parts[i].dev_pitch, parts[i].width,
+                                        parts[i].height, stream));
+        if (s) return s;
+        dst += parts[i].width * parts[i].height;
+    }
+    return KIVI_OK;
+}
+
+int kivi_stream_restore(const kivi_config* cfg, kivi_stream* st, const void* host, int64_t host_bytes,
+                        int64_t n_quant, int64_t ring_head, int64_t ring_count, void* stream) {
+    int s = check_config(cfg);
+    if (s) return s;
+    s = check_stream(cfg, st, false);
+    if (s) return s;
+    const int64_t G = cfg->group_size, slots = int64_t(cfg->residual_length) + G;
+    if (n_quant < 0 || n_quant % G != 0) return KIVI_E_STATE;
+    if (n_quant > st->cap_tokens) return KIVI_E_CAPACITY;
+    if (ring_head < 0 || ring_head >= slots || ring_count < 0 || ring_count > slots - 1) return KIVI_E_STATE;
+    if (st->n_slices > 0) {
+        ImagePart parts[8];
+        int64_t total = 0;
+        if (!image_parts(cfg, st->n_slices, n_quant, st->cap_tokens, parts, &total)) return KIVI_E_SHAPE;
+        if (host_bytes < total) return KIVI_E_SHAPE;
+        if (!host) return KIVI_E_NULL;
+        void* dst[8] = {st->k_codes, st->k_scale, st->k_zero, st->v_codes,
+                        st->v_scale, st->v_zero,  st->k_ring, st->v_ring};
+        const char* src = static_cast<const char*>(host);
+        for (int i = 0; i < 8; ++i) {
+            s = record(kivi::launch_copy_2d(dst[i], parts[i].dev_pitch, src, parts[i].width, parts[i].width,
+                                            parts[i].height, stream));
+            if (s) return s;
+            src += parts[i].width * parts[i].height;
+        }
+        // value rows of the residual tokens, re-quantized from the ring in at
+        // most two contiguous runs of slots (below the capacity only)
+        const int64_t D = cfg->head_dim, ngv = v_groups(cfg);
+        const int64_t wpt = ngv * (G * cfg->v_bits / 32);
+        int64_t todo = ring_count < st->cap_tokens - n_quant ? ring_count : st->cap_tokens - n_quant;
+        int64_t slot = ring_head, row = n_quant;
+        while (todo > 0) {
+            const int64_t run = todo < slots - slot ? todo : slots - slot;
+            kivi::EncodeArgs a;
+            a.in = static_cast<const uint16_t*>(st->v_ring) + slot * D;
+            a.in_stride = slots * D;
+            a.n_slices = st->n_slices;
+            a.n_tokens = static_cast<int32_t>(run);
+            a.cap_tokens = static_cast<int32_t>(st->cap_tokens);
+            a.head_dim = cfg->head_dim;
+            a.group_size = cfg->group_size;
+            a.bits = cfg->v_bits;
+            a.codes = reinterpret_cast<uint32_t*>(st->v_codes) + row * wpt;
+            a.scale = static_cast<uint16_t*>(st->v_scale) + row * ngv;
+            a.zero = static_cast<uint16_t*>(st->v_zero) + row * ngv;
+            s = record(kivi::launch_encode_v(a, stream));
+            if (s) return s;
+            todo -= run;
+            row += run;
+            slot = 0;
+        }
+    }
+    st->n_quant = n_quant;
+    st->ring_head = ring_head;
+    st->ring_count = ring_count;
+    return KIVI_OK;
 }
 
 }  // extern "C"

@@ -246,8 +246,12 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Acc<D>& ac
 // the attention kernel: blockIdx.x = slice * n_splits + split
 // ---------------------------------------------------------------------------
 
+// Register budget for 3 waves per SIMD where the compiler can meet it
+// (measured 5% faster than 2 at head_dim 128, 2/2-bit); the wider code
+// types stay at 2, which the compiler reports and this file accepts.
+#pragma clang diagnostic ignored "-Wpass-failed"
 template <int KB, int VB, int D>
-__global__ void __launch_bounds__(kWave) attention_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8))) attention_kernel(const AttnArgs a) {
     constexpr int NK32 = D / 32, NT16 = D / 16;
     __shared__ Smem<KB, VB, D> sm;
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;

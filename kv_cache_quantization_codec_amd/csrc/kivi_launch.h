@@ -4,6 +4,7 @@
 // (0 = success) and enqueues work on `stream` only.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace kivi {
@@ -141,5 +142,8 @@ int launch_decode_v(const DecodeArgs& a, void* stream);
 int launch_append_flush(const StepArgs& a, void* stream);
 int launch_ring_fill(const RingFillArgs& a, void* stream);
 int launch_attention(const AttnArgs& a, void* stream);
+// height rows of width bytes, between any mix of host and device memory
+int launch_copy_2d(void* dst, size_t dst_pitch, const void* src, size_t src_pitch, size_t width,
+                   size_t height, void* stream);
 
 }  // namespace kivi
