@@ -358,6 +358,7 @@ def stream_bench(w, args):
                     + S * (ngv * (G * w.v_bits // 32) * 4 + 2 * ngv * 2))
     flush_bytes = algorithmic_bytes("k", "encode", S, G, D, G, w.k_bits)
     pct = lambda a, q: round(float(np.percentile(a, q)), 2) if len(a) else None
+    offload = offload_bench(w, cfg, st, cap, dev)
     return {
         "metric": "streaming decode step latency (append 1 token per slice; flush a group "
                   "when the fp16 residual exceeds R), 1 MI355X",
@@ -386,6 +387,60 @@ def stream_bench(w, args):
         "prefill_GBps": round(prefill_bytes / (prefill_ms * 1e-3) / 1e9, 1),
         "host_wall_steps_per_s": round(w.steps / wall, 1),
         "final_state": {"n_quant": st.n_quant, "residual": st.ring_count},
+        "offload_restore": offload,
+    }
+
+
+def offload_bench(w, cfg, st, cap, dev):
+    """Compact host image of the streaming cache after the decode steps:
+    device-to-host offload and host-to-device restore (into a second stream)
+    through pinned memory, timed with HIP events, against a plain fp16 copy
+    of the same tokens' size class over the same link."""
+    import torch
+
+    import kv_cache_quantization_codec_amd as K
+
+    S, D = w.slices, w.head_dim
+    nbytes = K.kivi_stream_image_bytes(cfg, S, st.n_quant)
+    host = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    dst = K.Stream(cfg, S, cap, dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    off_ms = timed(lambda: K.kivi_stream_offload(st, host))
+    res_ms = timed(lambda: K.kivi_stream_restore(dst, host, st.n_quant, st.ring_head, st.ring_count))
+    # the same link moving fp16: a 2 GiB device -> pinned host copy, and back
+    probe = torch.empty(1 << 30, dtype=torch.float16, device=dev)
+    hprobe = torch.empty(1 << 30, dtype=torch.float16).pin_memory()
+    d2h_ms = timed(lambda: hprobe.copy_(probe, non_blocking=True))
+    h2d_ms = timed(lambda: probe.copy_(hprobe, non_blocking=True))
+    tokens = st.n_quant + st.ring_count
+    fp16_bytes = 2 * S * tokens * D * 2
+    d2h_gbps = probe.numel() * 2 / (d2h_ms * 1e-3) / 1e9
+    h2d_gbps = probe.numel() * 2 / (h2d_ms * 1e-3) / 1e9
+    return {
+        "what": "host image of the whole streaming cache (quantized prefix + fp16 residual ring) "
+                "through pinned memory; restore includes re-quantizing the residual value rows",
+        "cached_tokens": tokens,
+        "image_bytes": nbytes,
+        "fp16_bytes": fp16_bytes,
+        "compression": round(fp16_bytes / nbytes, 3),
+        "offload_ms": round(off_ms, 3),
+        "restore_ms": round(res_ms, 3),
+        "offload_link_GBps": round(nbytes / (off_ms * 1e-3) / 1e9, 2),
+        "restore_link_GBps": round(nbytes / (res_ms * 1e-3) / 1e9, 2),
+        "offload_fp16_equiv_GBps": round(fp16_bytes / (off_ms * 1e-3) / 1e9, 2),
+        "restore_fp16_equiv_GBps": round(fp16_bytes / (res_ms * 1e-3) / 1e9, 2),
+        "fp16_copy_d2h_GBps": round(d2h_gbps, 2),
+        "fp16_copy_h2d_GBps": round(h2d_gbps, 2),
     }
 
 
