@@ -12,6 +12,8 @@ Two tiers, written independently of each other and of the HIP path:
   for tiny inputs.  It pins the numpy tier's use of hardware rounding.
 * :mod:`oracle.attention_ref` -- float64 decode-phase attention of one query
   token per head over the dequantized prefix plus the fp16 residual.
+* :mod:`oracle.fp8_ref` -- FP8 (E4M3) keys of the k8v4 layout, by nearest
+  value over the listed code points.
 
 Sources (titles of the pages the method is taken from):
 
@@ -32,4 +34,4 @@ The pages print no formula for the statistics or the rounding; the readings
 used here are stated in each function's docstring.
 """
 
-from . import attention_ref, kivi_exact, kivi_ref  # noqa: F401
+from . import attention_ref, fp8_ref, kivi_exact, kivi_ref  # noqa: F401
