@@ -225,6 +225,31 @@ int kivi_stream_prefill(const kivi_config* cfg, kivi_stream* st,
 int kivi_append_flush(const kivi_config* cfg, kivi_stream* st,
                       const void* k_new_fp16, const void* v_new_fp16, void* hip_stream);
 
+/* FP8 keys of the k8v4 layout (vLLM turboquant/config.py: the
+ * turboquant_k8v4 preset stores keys in 8 bits and values in 4; its
+ * TurboQuantConfig docstring makes 8-bit keys FP8 with no rotation or
+ * codebook, and key_packed_size counts one byte per element with no
+ * overhead, i.e. a plain cast).  The values of that layout are
+ * kivi_encode_v with group_size = head_dim (one scale and zero per value
+ * vector, value_packed_size).  The page names neither the FP8 variant nor
+ * its rounding; the library uses OCP E4M3 (bias 7, 3 mantissa bits,
+ * subnormals, largest finite 448, NaN only at S.1111.111), round to nearest
+ * with ties to the even code, saturation to +-448, sign kept.
+ *   kivi_fp8_encode  fp16 [n_slices][in_slice_stride] -> codes uint8
+ *                    [n_slices][out_slice_stride]; token t of a slice
+ *                    occupies elements t*D .. t*D + D - 1 of both.
+ *   kivi_fp8_decode  codes -> fp16 (exact; every E4M3 value is an fp16
+ *                    value), same addressing.
+ * head_dim: a multiple of 8 in [8, 256] (KIVI_E_HEAD_DIM); strides at least
+ * n_tokens*D and multiples of 16 elements (KIVI_E_SHAPE / KIVI_E_ALIGN);
+ * pointers 16-byte aligned.  NaN and infinite inputs are out of contract. */
+int kivi_fp8_encode(const void* in_fp16, int64_t n_slices, int64_t n_tokens, int64_t head_dim,
+                    int64_t in_slice_stride, uint8_t* out, int64_t out_slice_stride,
+                    void* hip_stream);
+int kivi_fp8_decode(const uint8_t* in, int64_t n_slices, int64_t n_tokens, int64_t head_dim,
+                    int64_t in_slice_stride, void* out_fp16, int64_t out_slice_stride,
+                    void* hip_stream);
+
 /* Compact host image of a streaming cache (CacheSeek PR #4 "Feature
  * (quantization): add KIVI KV-cache quantization for exact-prefix reuse":
  * encoding runs on the source device, only the compact qdata/scale/offset

@@ -19,6 +19,8 @@ from .binding import (  # noqa: E402,F401
     kivi_decode_v,
     kivi_encode_k,
     kivi_encode_v,
+    kivi_fp8_decode,
+    kivi_fp8_encode,
     kivi_k_code_words,
     kivi_k_stat_elems,
     kivi_ring_elems,

@@ -78,6 +78,8 @@ SIGNATURES = [
     ("kivi_decode_v", _I32, [_CFG, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     ("kivi_stream_prefill", _I32, [_CFG, _ST, _P, _P, _I64, _I64, _P]),
     ("kivi_append_flush", _I32, [_CFG, _ST, _P, _P, _P]),
+    ("kivi_fp8_encode", _I32, [_P, _I64, _I64, _I64, _I64, _P, _I64, _P]),
+    ("kivi_fp8_decode", _I32, [_P, _I64, _I64, _I64, _I64, _P, _I64, _P]),
     ("kivi_stream_image_bytes", _I64, [_CFG, _I64, _I64]),
     ("kivi_stream_offload", _I32, [_CFG, _ST, _P, _I64, _P]),
     ("kivi_stream_restore", _I32, [_CFG, _ST, _P, _I64, _I64, _I64, _I64, _P]),
@@ -292,6 +294,37 @@ def kivi_append_flush(st: Stream, k_new: torch.Tensor, v_new: torch.Tensor, stre
     _check(lib().kivi_append_flush(_cfg(st.cfg), ctypes.byref(st.state), _ptr(k_new), _ptr(v_new),
                                    _stream_ptr(stream)), "kivi_append_flush")
     return st.state.n_quant != before
+
+
+# ---------------------------------------------------------------------------
+# FP8 keys (k8v4 layout)
+# ---------------------------------------------------------------------------
+
+def _rows(t: torch.Tensor, dtype, what: str):
+    """(n_slices, n_rows_allocated, D, slice_stride) of a [S, T, D] tensor with contiguous rows."""
+    if t.dtype != dtype or t.dim() != 3 or t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+        raise ValueError(f"{what}: expected {dtype} [S, T, D] with contiguous token rows")
+    return t.shape[0], t.shape[1], t.shape[2], t.stride(0)
+
+
+def kivi_fp8_encode(k: torch.Tensor, n_tokens: int, out: torch.Tensor, stream=None):
+    """FP8 (E4M3) codes of tokens [0, n_tokens) of ``k`` fp16 [S, T, D] into
+    ``out`` uint8 [S, T', D]."""
+    S, _, D, si = _rows(k, torch.float16, "k")
+    S2, _, D2, so = _rows(out, torch.uint8, "out")
+    if (S2, D2) != (S, D):
+        raise ValueError("out must match k's slices and head_dim")
+    _check(lib().kivi_fp8_encode(_ptr(k), S, n_tokens, D, si, _ptr(out), so, _stream_ptr(stream)),
+           "kivi_fp8_encode")
+
+
+def kivi_fp8_decode(codes: torch.Tensor, n_tokens: int, out: torch.Tensor, stream=None):
+    S, _, D, si = _rows(codes, torch.uint8, "codes")
+    S2, _, D2, so = _rows(out, torch.float16, "out")
+    if (S2, D2) != (S, D):
+        raise ValueError("out must match the codes' slices and head_dim")
+    _check(lib().kivi_fp8_decode(_ptr(codes), S, n_tokens, D, si, _ptr(out), so, _stream_ptr(stream)),
+           "kivi_fp8_decode")
 
 
 # ---------------------------------------------------------------------------

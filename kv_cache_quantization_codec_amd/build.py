@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkivi.so")
 
 SOURCES = [os.path.join(CSRC, "kivi_api.cpp"), os.path.join(CSRC, "kivi_kernels.hip"),
-           os.path.join(CSRC, "kivi_attention.hip"), os.path.join(CSRC, "kivi_copy.hip")]
+           os.path.join(CSRC, "kivi_attention.hip"), os.path.join(CSRC, "kivi_copy.hip"),
+           os.path.join(CSRC, "kivi_fp8.hip")]
 
 FLAGS = [
     "--offload-arch=gfx950",

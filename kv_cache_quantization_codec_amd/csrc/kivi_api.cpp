@@ -551,4 +551,43 @@ int kivi_stream_restore(const kivi_config* cfg, kivi_stream* st, const void* hos
     return KIVI_OK;
 }
 
+namespace {
+
+int fp8_call(bool enc, const void* in, int64_t n_slices, int64_t n_tokens, int64_t D, int64_t in_stride,
+             void* out, int64_t out_stride, void* stream) {
+    if (D < 8 || D > 256 || D % 8 != 0) return KIVI_E_HEAD_DIM;
+    if (n_slices < 0 || n_tokens < 0 || n_tokens > kMaxTokens) return KIVI_E_SHAPE;
+    if (n_tokens * (D / 8) > (int64_t(1) << 30)) return KIVI_E_SHAPE;   // 32-bit chunk index per slice
+    if (n_slices == 0 || n_tokens == 0) return KIVI_OK;
+    if (in_stride % 16 != 0 || out_stride % 16 != 0) return KIVI_E_ALIGN;
+    int64_t need = 0, total = 0;
+    if (!mul_ok(n_tokens, D, &need) || in_stride < need || out_stride < need) return KIVI_E_SHAPE;
+    if (!mul_ok(n_slices, in_stride, &total) || !mul_ok(n_slices, out_stride, &total) ||
+        !mul_ok(total, 2, &total))
+        return KIVI_E_SHAPE;
+    if (!in || !out) return KIVI_E_NULL;
+    if (!aligned16(in) || !aligned16(out)) return KIVI_E_ALIGN;
+    kivi::Fp8Args a;
+    a.in = in;
+    a.in_stride = in_stride;
+    a.out = out;
+    a.out_stride = out_stride;
+    a.n_slices = n_slices;
+    a.n_tokens = static_cast<int32_t>(n_tokens);
+    a.head_dim = static_cast<int32_t>(D);
+    return record(enc ? kivi::launch_fp8_encode(a, stream) : kivi::launch_fp8_decode(a, stream));
+}
+
+}  // namespace
+
+int kivi_fp8_encode(const void* in, int64_t n_slices, int64_t n_tokens, int64_t head_dim,
+                    int64_t in_stride, uint8_t* out, int64_t out_stride, void* stream) {
+    return fp8_call(true, in, n_slices, n_tokens, head_dim, in_stride, out, out_stride, stream);
+}
+
+int kivi_fp8_decode(const uint8_t* in, int64_t n_slices, int64_t n_tokens, int64_t head_dim,
+                    int64_t in_stride, void* out, int64_t out_stride, void* stream) {
+    return fp8_call(false, in, n_slices, n_tokens, head_dim, in_stride, out, out_stride, stream);
+}
+
 }  // extern "C"

@@ -135,6 +135,18 @@ struct AttnArgs {
     AttnPlan plan;
 };
 
+// FP8 key cast: in/out element strides between slices (fp16 elements or
+// code bytes); token rows of head_dim elements.
+struct Fp8Args {
+    const void* in;
+    int64_t in_stride;
+    void* out;
+    int64_t out_stride;
+    int64_t n_slices;
+    int32_t n_tokens;
+    int32_t head_dim;
+};
+
 int launch_encode_k(const EncodeArgs& a, void* stream);
 int launch_encode_v(const EncodeArgs& a, void* stream);
 int launch_decode_k(const DecodeArgs& a, void* stream);
@@ -142,6 +154,8 @@ int launch_decode_v(const DecodeArgs& a, void* stream);
 int launch_append_flush(const StepArgs& a, void* stream);
 int launch_ring_fill(const RingFillArgs& a, void* stream);
 int launch_attention(const AttnArgs& a, void* stream);
+int launch_fp8_encode(const Fp8Args& a, void* stream);
+int launch_fp8_decode(const Fp8Args& a, void* stream);
 // height rows of width bytes, between any mix of host and device memory
 int launch_copy_2d(void* dst, size_t dst_pitch, const void* src, size_t src_pitch, size_t width,
                    size_t height, void* stream);
