@@ -249,6 +249,8 @@ def cpu_baseline(k, v, w, cfg, n, budget_s=12.0):
 
     from oracle import kivi_ref as ref
 
+    from oracle import fp8_ref as f8
+
     G = cfg.group_size
     done = 0
     spent = 0.0
@@ -259,9 +261,12 @@ def cpu_baseline(k, v, w, cfg, n, budget_s=12.0):
         kh = k[sl].cpu().numpy()
         vh = v[sl].cpu().numpy()
         t0 = time.perf_counter()
-        kc, ks, kz = ref.encode_k(kh, n, cfg.k_bits, G)
+        if w.fp8_keys:
+            f8.decode(f8.encode_keys(kh, n))
+        else:
+            kc, ks, kz = ref.encode_k(kh, n, cfg.k_bits, G)
+            ref.decode_k(kc, ks, kz, n, cfg.k_bits, G)
         vc, vs, vz = ref.encode_v(vh, n, cfg.v_bits, G)
-        ref.decode_k(kc, ks, kz, n, cfg.k_bits, G)
         ref.decode_v(vc, vs, vz, n, cfg.v_bits, G, cfg.head_dim)
         spent += time.perf_counter() - t0
         done = sl.stop
@@ -451,7 +456,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama2_7b_2bit",
                     choices=["llama2_7b_2bit", "mistral_7b_k2v4", "single_layer_4bit",
-                             "stream_b64"])
+                             "llama2_7b_k8v4", "stream_b64"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-ceiling", action="store_true",
@@ -497,19 +502,27 @@ def main():
         k[layer * spl:(layer + 1) * spl] = kl
         v[layer * spl:(layer + 1) * spl] = vl
         del kl, vl
-    kq = K.alloc_keys(cfg, S, n, dev)
     vq = K.alloc_values(cfg, S, n, dev)
     ko = torch.empty((S, n, D), dtype=torch.float16, device=dev)
     vo = torch.empty_like(ko)
-    torch.cuda.synchronize()
-
     names = ["encode_k", "encode_v", "decode_k", "decode_v"]
-    calls = [
-        lambda: K.kivi_encode_k(cfg, k, n, *kq),
-        lambda: K.kivi_encode_v(cfg, v, n, *vq),
-        lambda: K.kivi_decode_k(cfg, *kq, n, ko),
-        lambda: K.kivi_decode_v(cfg, *vq, n, vo),
-    ]
+    if w.fp8_keys:
+        kq = torch.empty((S, n, D), dtype=torch.uint8, device=dev)
+        calls = [
+            lambda: K.kivi_fp8_encode(k, n, kq),
+            lambda: K.kivi_encode_v(cfg, v, n, *vq),
+            lambda: K.kivi_fp8_decode(kq, n, ko),
+            lambda: K.kivi_decode_v(cfg, *vq, n, vo),
+        ]
+    else:
+        kq = K.alloc_keys(cfg, S, n, dev)
+        calls = [
+            lambda: K.kivi_encode_k(cfg, k, n, *kq),
+            lambda: K.kivi_encode_v(cfg, v, n, *vq),
+            lambda: K.kivi_decode_k(cfg, *kq, n, ko),
+            lambda: K.kivi_decode_v(cfg, *vq, n, vo),
+        ]
+    torch.cuda.synchronize()
     for _ in range(args.warmup):
         for c in calls:
             c()
@@ -532,6 +545,8 @@ def main():
     fp16_eq = 2 * 2 * S * n * D * 2                  # K and V, encode + decode
     bits = {"encode_k": w.k_bits, "decode_k": w.k_bits, "encode_v": w.v_bits, "decode_v": w.v_bits}
     alg = {nm: algorithmic_bytes(nm[-1], nm[:6], S, n, D, G, bits[nm]) for nm in names}
+    if w.fp8_keys:                                    # 2 bytes in, 1 out (and back)
+        alg["encode_k"] = alg["decode_k"] = 3 * S * n * D
     moved = sum(alg.values())
     dom = max(names, key=lambda nm: per_kernel_ms[nm])
     achieved = alg[dom] / (per_kernel_ms[dom] / 1000.0) / 1e9
@@ -556,6 +571,7 @@ def main():
             "layers": w.layers, "batch": w.batch, "kv_heads": w.heads, "head_dim": D,
             "seq_len": T, "quantized_tokens": n, "residual_length": w.residual_length,
             "k_bits": w.k_bits, "v_bits": w.v_bits, "group_size": G,
+            "key_format": "fp8_e4m3" if w.fp8_keys else "kivi",
         },
         "moved_GBps": round(moved / (ms_step / 1000.0) / 1e9, 2),
         "hbm_roofline_frac_step": round(moved / (ms_step / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -573,7 +589,8 @@ def main():
             "algorithmic_bytes_per_launch": alg[dom],
         },
     }
-    out["attention"] = attention_bench(w, cfg, k, v, kq, vq, n, args, dev)
+    if not w.fp8_keys:
+        out["attention"] = attention_bench(w, cfg, k, v, kq, vq, n, args, dev)
     if args.copy_ceiling:
         out["copy_ceiling_GBps"] = copy_ceiling(dev)
     if not args.no_cpu_baseline:

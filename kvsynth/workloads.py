@@ -40,6 +40,7 @@ class Workload:
     residual_length: int
     steps: int = 0          # streaming decode steps (0 = full-cache encode)
     q_per_kv: int = 1       # query heads per KV head at decode (grouped-query attention)
+    fp8_keys: bool = False  # k8v4 layout: FP8 keys, values with one group per head
 
     @property
     def slices_per_layer(self) -> int:
@@ -57,6 +58,8 @@ WORKLOADS = {
                                32, 8, 32, 4096, 128, 2, 2, 32, 128),
     "mistral_7b_k2v4": Workload(3, "Mistral-7B-shaped GQA cache, batch 16, 16384 tokens, K2/V4",
                                 32, 16, 8, 16384, 128, 2, 4, 32, 128, q_per_kv=4),
+    "llama2_7b_k8v4": Workload(5, "Llama-2-7B-shaped cache, batch 8, 4096 tokens, FP8 keys + 4-bit values",
+                               32, 8, 32, 4096, 128, 8, 4, 128, 128, fp8_keys=True),
     "stream_b64": Workload(4, "streaming decode, batch 64, prefill 2048 + 512 steps, 2/2-bit",
                            32, 64, 8, 2048, 128, 2, 2, 32, 128, steps=512),
 }
