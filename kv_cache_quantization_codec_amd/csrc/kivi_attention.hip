@@ -200,11 +200,14 @@ __device__ __forceinline__ void weights_to_lds(SM& sm, const float pa[2], const 
     }
     lds_order();
     const int t = L & 31;
-    for (int h = L >> 5; h < r; h += 2) {
-        f16 hi, lo;
-        split_hl(sm.pp[h][t], hi, lo);
-        sm.apz[2 * h][t] = hi;
-        sm.apz[2 * h + 1][t] = lo;
+    for (int h0 = 0; h0 < r; h0 += 2) {
+        const int h = h0 + (L >> 5);
+        if (h < r) {
+            f16 hi, lo;
+            split_hl(sm.pp[h][t], hi, lo);
+            sm.apz[2 * h][t] = hi;
+            sm.apz[2 * h + 1][t] = lo;
+        }
     }
     lds_order();
 }
@@ -250,12 +253,12 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Acc<D>& ac
 // (measured 5% faster than 2 at head_dim 128, 2/2-bit); the wider code
 // types stay at 2, which the compiler reports and this file accepts.
 #pragma clang diagnostic ignored "-Wpass-failed"
-template <int KB, int VB, int D>
+template <int KB, int VB, int D, int G>
 __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8))) attention_kernel(const AttnArgs a) {
     constexpr int NK32 = D / 32, NT16 = D / 16;
     __shared__ Smem<KB, VB, D> sm;
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
-    const int G = a.group_size, r = a.q_per_kv;
+    const int r = a.q_per_kv;
     const int64_t s = blockIdx.x / a.plan.n_splits;
     const int split = (int)(blockIdx.x - s * a.plan.n_splits);
     const bool residual = a.plan.has_res && split == a.plan.n_splits - 1;
@@ -354,10 +357,11 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     const int b0 = split * a.plan.blocks_per_split;
     const int b1 = min(b0 + a.plan.blocks_per_split, a.plan.n_blocks);
     const int n = a.n_quant;
-    const int Wk = G * KB / 32;                           // key words per channel per group
+    constexpr int Wk = G * KB / 32;                       // key words per channel per group
+    constexpr int NGV = (D + G - 1) / G;                  // value groups per row
+    constexpr int WPT = NGV * G * VB / 32;                // value words per row
     const int ngk_cap = (a.cap_tokens + G - 1) / G;
-    const int ngv = (D + G - 1) / G;
-    const int wpt = ngv * G * VB / 32;                    // value words per row
+    const int ngv = NGV, wpt = WPT;
     constexpr int VPAIRS = D * VB / 64;                   // word pairs per row that hold real channels
     const uint32_t* kcs = a.k_codes + s * (int64_t)ngk_cap * Wk * D;
     const uint16_t* kss = a.k_scale + s * (int64_t)ngk_cap * D;
@@ -375,7 +379,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     struct Stage {
         u32x4 k[KV];
         uint32_t v[VV][2];
-        uint16_t vsb[2], vzb[2];
+        uint16_t vsb[(32 * NGV + kWave - 1) / kWave], vzb[(32 * NGV + kWave - 1) / kWave];
         uint32_t ks, kz;
     };
     auto load = [&](int blk, Stage& st) {
@@ -384,31 +388,27 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
 #pragma unroll
         for (int i = 0; i < KV; ++i) {
             const int v = L + kWave * i;
-            if (v < KCH) st.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(srck) + v);
+            if (KCH % kWave == 0 || v < KCH) st.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(srck) + v);
         }
 #pragma unroll
         for (int i = 0; i < VV; ++i) {
             const int e = L + kWave * i;
-            st.v[i][0] = st.v[i][1] = 0;
-            if (e < 32 * VPAIRS) {
+            if (32 * VPAIRS % kWave == 0 || e < 32 * VPAIRS) {
                 const int row = e / VPAIRS, c2 = 2 * (e - row * VPAIRS);
-                if (t0 + row < n) {
-                    const uint32_t* src = vcs + (int64_t)(t0 + row) * wpt + c2;
-                    st.v[i][0] = __builtin_nontemporal_load(src);
-                    st.v[i][1] = __builtin_nontemporal_load(src + 1);
-                }
+                const int t = min(t0 + row, n - 1);       // rows past n: masked at commit
+                const uint32_t* src = vcs + (int64_t)t * WPT + c2;
+                st.v[i][0] = __builtin_nontemporal_load(src);
+                st.v[i][1] = __builtin_nontemporal_load(src + 1);
             }
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < (32 * NGV + kWave - 1) / kWave; ++i) {
             const int e = L + kWave * i;
-            st.vsb[i] = st.vzb[i] = 0;
-            if (e < 32 * ngv) {
-                const int row = e / ngv, gv = e - row * ngv;
-                if (t0 + row < n) {
-                    st.vsb[i] = vss[(int64_t)(t0 + row) * ngv + gv];
-                    st.vzb[i] = vzs[(int64_t)(t0 + row) * ngv + gv];
-                }
+            if (32 * NGV % kWave == 0 || e < 32 * NGV) {
+                const int row = e / NGV, gv = e - row * NGV;
+                const int t = min(t0 + row, n - 1);       // rows past n: any valid row, masked below
+                st.vsb[i] = vss[(int64_t)t * NGV + gv];
+                st.vzb[i] = vzs[(int64_t)t * NGV + gv];
             }
         }
         if ((t0 % G == 0 || blk == b0) && pair_live) {
@@ -421,7 +421,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
 #pragma unroll
         for (int i = 0; i < KV; ++i) {
             const int v = L + kWave * i;
-            if (v < KCH) {
+            if (KCH % kWave == 0 || v < KCH) {
                 const int row = (4 * v) / D, col = (4 * v) % D;
                 *reinterpret_cast<u32x4*>(&sm.kc[row][col]) = st.k[i];
             }
@@ -429,19 +429,21 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
 #pragma unroll
         for (int i = 0; i < VV; ++i) {
             const int e = L + kWave * i;
-            if (e < 32 * VPAIRS) {
+            if (32 * VPAIRS % kWave == 0 || e < 32 * VPAIRS) {
                 const int row = e / VPAIRS, c2 = 2 * (e - row * VPAIRS);
-                sm.vc[c2][row] = st.v[i][0];
-                sm.vc[c2 + 1][row] = st.v[i][1];
+                const bool live = t0 + row < n;
+                sm.vc[c2][row] = live ? st.v[i][0] : 0u;
+                sm.vc[c2 + 1][row] = live ? st.v[i][1] : 0u;
             }
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < (32 * NGV + kWave - 1) / kWave; ++i) {
             const int e = L + kWave * i;
-            if (e < 32 * ngv) {
-                const int row = e / ngv, gv = e - row * ngv;
-                sm.vs[gv][row] = (float)__builtin_bit_cast(f16, st.vsb[i]);
-                sm.vz[gv][row] = __builtin_bit_cast(f16, st.vzb[i]);
+            if (32 * NGV % kWave == 0 || e < 32 * NGV) {
+                const int row = e / NGV, gv = e - row * NGV;
+                const bool live = t0 + row < n;
+                sm.vs[gv][row] = live ? (float)__builtin_bit_cast(f16, st.vsb[i]) : 0.0f;
+                sm.vz[gv][row] = __builtin_bit_cast(f16, live ? st.vzb[i] : (uint16_t)0);
             }
         }
         // a new key group: q*s operand rows (fp32 product split hi/lo) and zeros
@@ -507,13 +509,17 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         // values: the p*s operand of every value group
         {
             const int t = L & 31;
-            for (int h = L >> 5; h < r; h += 2) {
-                const float p = sm.pp[h][t];
-                for (int gv = 0; gv < ngv; ++gv) {
-                    f16 hi, lo;
-                    split_hl(p * sm.vs[gv][t], hi, lo);
-                    sm.ap[gv][2 * h][t] = hi;
-                    sm.ap[gv][2 * h + 1][t] = lo;
+            for (int h0 = 0; h0 < r; h0 += 2) {
+                const int h = h0 + (L >> 5);
+                if (h < r) {
+                    const float p = sm.pp[h][t];
+#pragma unroll
+                    for (int gv = 0; gv < NGV; ++gv) {
+                        f16 hi, lo;
+                        split_hl(p * sm.vs[gv][t], hi, lo);
+                        sm.ap[gv][2 * h][t] = hi;
+                        sm.ap[gv][2 * h + 1][t] = lo;
+                    }
                 }
             }
         }
@@ -574,10 +580,10 @@ __global__ void __launch_bounds__(kWave) attention_merge_kernel(const AttnArgs a
     if (L + kWave < D) dst[L + kWave] = __builtin_bit_cast(uint16_t, (f16)(o1 * inv));
 }
 
-template <int KB, int VB, int D>
+template <int KB, int VB, int D, int G>
 int run_attention(const AttnArgs& a, hipStream_t st) {
     const int64_t groups = a.n_slices * a.plan.n_splits;
-    hipLaunchKernelGGL((attention_kernel<KB, VB, D>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
+    hipLaunchKernelGGL((attention_kernel<KB, VB, D, G>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (a.plan.n_splits > 1) {
@@ -593,13 +599,20 @@ int run_attention(const AttnArgs& a, hipStream_t st) {
 int launch_attention(const AttnArgs& a, void* stream) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (a.n_slices == 0) return 0;
+#define KIVI_ATTN_G(KB, VB, D)                                                         \
+    switch (a.group_size) {                                                            \
+        case 32: return run_attention<KB, VB, D, 32>(a, st);                           \
+        case 64: return run_attention<KB, VB, D, 64>(a, st);                           \
+        case 128: return run_attention<KB, VB, D, 128>(a, st);                         \
+        default: return (int)hipErrorInvalidValue;                                     \
+    }
 #define KIVI_ATTN(KB, VB)                                                              \
     if (a.k_bits == KB && a.v_bits == VB) {                                            \
         switch (a.head_dim) {                                                          \
-            case 32: return run_attention<KB, VB, 32>(a, st);                          \
-            case 64: return run_attention<KB, VB, 64>(a, st);                          \
-            case 96: return run_attention<KB, VB, 96>(a, st);                          \
-            case 128: return run_attention<KB, VB, 128>(a, st);                        \
+            case 32: KIVI_ATTN_G(KB, VB, 32)                                           \
+            case 64: KIVI_ATTN_G(KB, VB, 64)                                           \
+            case 96: KIVI_ATTN_G(KB, VB, 96)                                           \
+            case 128: KIVI_ATTN_G(KB, VB, 128)                                         \
             default: return (int)hipErrorInvalidValue;                                 \
         }                                                                              \
     }
@@ -607,6 +620,7 @@ int launch_attention(const AttnArgs& a, void* stream) {
     KIVI_ATTN(4, 2) KIVI_ATTN(4, 4) KIVI_ATTN(4, 8)
     KIVI_ATTN(8, 2) KIVI_ATTN(8, 4) KIVI_ATTN(8, 8)
 #undef KIVI_ATTN
+#undef KIVI_ATTN_G
     return (int)hipErrorInvalidValue;
 }
 
