@@ -130,20 +130,23 @@ __device__ __forceinline__ void split_hl(float x, f16& hi, f16& lo) {
     lo = (f16)(x - (float)hi);
 }
 
-// LDS of one wave (D = head_dim).  Row strides are padded by 16 bytes so
-// that the 16 rows an MFMA operand read touches fall in different banks.
-template <int KB, int VB, int D>
+// LDS of one wave (D = head_dim, at most RMAX query heads per KV slice, so
+// 2*RMAX live MFMA rows; lanes of the other rows use zero operands without
+// reading LDS).  Row strides are padded by 16 bytes so that the rows an
+// MFMA operand read touches fall in different banks.  Sizing the rows by
+// RMAX keeps the multi-head case small enough for LDS not to limit the
+// number of resident waves.
+template <int KB, int VB, int D, int RMAX>
 struct alignas(16) Smem {
-    f16 q[8][D + 8];                       // the slice's queries, one row per head
-    f16 aq[16][D + 8];                     // q*s of the current key group, hi/lo rows
+    f16 q[RMAX][D + 8];                    // the slice's queries, one row per head
+    f16 aq[2 * RMAX][D + 8];               // q*s of the current key group, hi/lo rows
     f16 kz[D];                             // zeros of the current key group
     uint32_t kc[KB][D];                    // key codes of a 32-token block
     uint32_t vc[VB * D / 32][kVcStride];   // value codes, [word column][row]
     f16 vz[4][kTokStride];                 // value zeros, [group][row]
     float vs[4][32 + 4];                   // value scales, [group][row]
-    float pp[8][32 + 4];                   // softmax weights, [head][token]
-    f16 ap[4][16][kTokStride];             // p*s per value group, hi/lo rows
-    f16 apz[16][kTokStride];               // p, hi/lo rows
+    f16 ap[4][2 * RMAX][kTokStride];       // p*s per value group, hi/lo rows
+    f16 apz[2 * RMAX][kTokStride];         // p, hi/lo rows
 };
 
 // Per-wave running softmax state and output accumulators for the two heads
@@ -188,25 +191,22 @@ __device__ __forceinline__ void softmax_block(Acc<D>& acc, float xa[2], float xb
     acc.z[3] *= al_b;
 }
 
-// Softmax weights of the block to LDS ([head][token]) and, as hi/lo fp16
-// rows, to the operand apz ([2h / 2h+1][token]).
+// The block's softmax weights (this lane: tokens 16tt + j of heads 2kq and
+// 2kq+1) as hi/lo fp16 rows of the value operand apz ([2h / 2h+1][token]).
 template <class SM>
 __device__ __forceinline__ void weights_to_lds(SM& sm, const float pa[2], const float pb[2], int r) {
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        sm.pp[2 * kq][16 * tt + j] = pa[tt];
-        sm.pp[2 * kq + 1][16 * tt + j] = pb[tt];
-    }
-    lds_order();
-    const int t = L & 31;
-    for (int h0 = 0; h0 < r; h0 += 2) {
-        const int h = h0 + (L >> 5);
+    for (int hh = 0; hh < 2; ++hh) {
+        const int h = 2 * kq + hh;
         if (h < r) {
-            f16 hi, lo;
-            split_hl(sm.pp[h][t], hi, lo);
-            sm.apz[2 * h][t] = hi;
-            sm.apz[2 * h + 1][t] = lo;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                f16 hi, lo;
+                split_hl(hh ? pb[tt] : pa[tt], hi, lo);
+                sm.apz[2 * h][16 * tt + j] = hi;
+                sm.apz[2 * h + 1][16 * tt + j] = lo;
+            }
         }
     }
     lds_order();
@@ -253,10 +253,10 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Acc<D>& ac
 // (measured 5% faster than 2 at head_dim 128, 2/2-bit); the wider code
 // types stay at 2, which the compiler reports and this file accepts.
 #pragma clang diagnostic ignored "-Wpass-failed"
-template <int KB, int VB, int D, int G>
+template <int KB, int VB, int D, int G, int RMAX>
 __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8))) attention_kernel(const AttnArgs a) {
-    constexpr int NK32 = D / 32, NT16 = D / 16;
-    __shared__ Smem<KB, VB, D> sm;
+    constexpr int NK32 = D / 32, NT16 = D / 16, ROWS = 2 * RMAX;
+    __shared__ Smem<KB, VB, D, RMAX> sm;
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
     const int r = a.q_per_kv;
     const int64_t s = blockIdx.x / a.plan.n_splits;
@@ -264,23 +264,26 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     const bool residual = a.plan.has_res && split == a.plan.n_splits - 1;
 
     // operand rows that are never written stay zero
-    for (int i = L; i < 16 * (D + 8); i += kWave) (&sm.aq[0][0])[i] = (f16)0;
-    for (int i = L; i < 4 * 16 * kTokStride; i += kWave) (&sm.ap[0][0][0])[i] = (f16)0;
-    for (int i = L; i < 16 * kTokStride; i += kWave) (&sm.apz[0][0])[i] = (f16)0;
+    for (int i = L; i < ROWS * (D + 8); i += kWave) (&sm.aq[0][0])[i] = (f16)0;
+    for (int i = L; i < 4 * ROWS * kTokStride; i += kWave) (&sm.ap[0][0][0])[i] = (f16)0;
+    for (int i = L; i < ROWS * kTokStride; i += kWave) (&sm.apz[0][0])[i] = (f16)0;
     // the queries to LDS; rows of heads >= r are zero
-    for (int i = L; i < D; i += kWave) {
+    for (int i = L; i < RMAX * D / 8; i += kWave) {
         const int h = i / (D / 8), c = 8 * (i - h * (D / 8));
         u32x4 w = u32x4{0, 0, 0, 0};
         if (h < r) w = *reinterpret_cast<const u32x4*>(a.q + (s * r + h) * D + c);
         *reinterpret_cast<u32x4*>(&sm.q[h][c]) = w;
     }
+    // A-operand rows: lane row j; rows >= ROWS are zero without an LDS read
+    const bool row_live = j < ROWS;
+    const int jr = row_live ? j : 0;
+    const h8 zero8 = __builtin_bit_cast(h8, u32x4{0, 0, 0, 0});
     // q as MFMA A operand, rows 2h = q_h and 2h+1 = 0: lane row j, channels
-    // 32*kk + 8*kq .. +7 (odd rows read a zero row of aq's initial state is not
-    // guaranteed, so they are masked)
-    const bool qrow_live = (j & 1) == 0;
+    // 32*kk + 8*kq .. +7
+    const bool qrow_live = (j & 1) == 0 && (j >> 1) < RMAX;
     auto qa = [&](int kk) {
-        const h8 v = lds_h8(&sm.q[j >> 1][32 * kk + 8 * kq]);
-        return qrow_live ? v : __builtin_bit_cast(h8, u32x4{0, 0, 0, 0});
+        const h8 v = lds_h8(&sm.q[qrow_live ? j >> 1 : 0][32 * kk + 8 * kq]);
+        return qrow_live ? v : zero8;
     };
 
     Acc<D> acc;
@@ -321,7 +324,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             softmax_block(acc, xa, xb);
             weights_to_lds(sm, xa, xb, r);
             // values: B[token 8kq+e][channel 16nt+j]
-            const h8 pa8 = lds_h8(&sm.apz[j][8 * kq]);
+            const h8 pa8 = row_live ? lds_h8(&sm.apz[jr][8 * kq]) : zero8;
             const uint16_t* vrow[8];
             bool valid[8];
 #pragma unroll
@@ -486,7 +489,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         f4 sc[2] = {f4{0, 0, 0, 0}, f4{0, 0, 0, 0}};
 #pragma unroll
         for (int kk = 0; kk < NK32; ++kk) {
-            const h8 aop = lds_h8(&sm.aq[j][32 * kk + 8 * kq]);
+            const h8 aop = row_live ? lds_h8(&sm.aq[jr][32 * kk + 8 * kq]) : zero8;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int wi = (16 * tt + j) / (32 / KB);
@@ -504,18 +507,24 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             xb[tt] = valid ? ((sc[tt][2] + sc[tt][3]) * kpos.col + zk[2]) * a.logit_scale : kNegInf;
         }
         softmax_block(acc, xa, xb);
-        weights_to_lds(sm, xa, xb, r);
 
-        // values: the p*s operand of every value group
-        {
-            const int t = L & 31;
-            for (int h0 = 0; h0 < r; h0 += 2) {
-                const int h = h0 + (L >> 5);
-                if (h < r) {
-                    const float p = sm.pp[h][t];
+        // values: each lane turns its own weights (tokens 16tt + j, heads
+        // 2kq and 2kq+1) into the hi/lo operand rows of p and of p*s for
+        // every value group, straight from registers
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int h = 2 * kq + hh;
+            if (h < r) {
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const int t = 16 * tt + j;
+                    const float p = hh ? xb[tt] : xa[tt];
+                    f16 hi, lo;
+                    split_hl(p, hi, lo);
+                    sm.apz[2 * h][t] = hi;
+                    sm.apz[2 * h + 1][t] = lo;
 #pragma unroll
                     for (int gv = 0; gv < NGV; ++gv) {
-                        f16 hi, lo;
                         split_hl(p * sm.vs[gv][t], hi, lo);
                         sm.ap[gv][2 * h][t] = hi;
                         sm.ap[gv][2 * h + 1][t] = lo;
@@ -526,14 +535,14 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         lds_order();
         // values: zero-point term over all groups at once (columns = groups)
         {
-            const h8 pz = lds_h8(&sm.apz[j][8 * kq]);
+            const h8 pz = row_live ? lds_h8(&sm.apz[jr][8 * kq]) : zero8;
             const h8 bz = lds_h8(&sm.vz[j < ngv ? j : 0][8 * kq]);
             acc.z = mfma(pz, j < ngv ? bz : __builtin_bit_cast(h8, u32x4{0, 0, 0, 0}), acc.z);
         }
 #pragma unroll
         for (int nt = 0; nt < NT16; ++nt) {
             const int gv = (16 * nt) / G;
-            const h8 aop = lds_h8(&sm.ap[gv][j][8 * kq]);
+            const h8 aop = row_live ? lds_h8(&sm.ap[gv][jr][8 * kq]) : zero8;
             const int col = (16 * nt + j) / (32 / VB);
             const uint32_t* wp = &sm.vc[col][8 * kq];
             const h8 bop = codes8<VB>(*reinterpret_cast<const u32x4*>(wp),
@@ -583,7 +592,10 @@ __global__ void __launch_bounds__(kWave) attention_merge_kernel(const AttnArgs a
 template <int KB, int VB, int D, int G>
 int run_attention(const AttnArgs& a, hipStream_t st) {
     const int64_t groups = a.n_slices * a.plan.n_splits;
-    hipLaunchKernelGGL((attention_kernel<KB, VB, D, G>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
+    if (a.q_per_kv <= 2)
+        hipLaunchKernelGGL((attention_kernel<KB, VB, D, G, 2>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
+    else
+        hipLaunchKernelGGL((attention_kernel<KB, VB, D, G, 8>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (a.plan.n_splits > 1) {
