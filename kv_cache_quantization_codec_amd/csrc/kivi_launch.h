@@ -89,7 +89,7 @@ struct AttnPlan {
 };
 
 inline AttnPlan attn_plan(int64_t n_slices, int64_t n_quant, int64_t res_count) {
-    const int64_t kTargetGroups = 8192;    // workgroups that keep 256 CUs busy
+    const int64_t kTargetGroups = 32768;   // several waves of resident workgroups (short tail)
     const int64_t kMinBlocks = 4;          // keep partial-sum traffic below ~5%
     AttnPlan p{};
     p.n_blocks = (int32_t)((n_quant + 31) / 32);
