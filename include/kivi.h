@@ -316,7 +316,16 @@ int kivi_stream_restore(const kivi_config* cfg, kivi_stream* st, const void* hos
  *                      ring_count; a full-cache encode of T tokens maps to
  *                      res_k = k + n_quant*D with the input's slice stride
  *                      and res_slots = res_count = T - n_quant, res_head = 0.
- *                      May be NULL when res_count == 0. */
+ *                      May be NULL when res_count == 0.
+ *   n_quant_per_slice, res_count_per_slice
+ *                      optional device arrays of n_slices int32 (NULL: every
+ *                      slice has n_quant quantized and res_count residual
+ *                      tokens).  Given, slice s has n_quant_per_slice[s]
+ *                      quantized and res_count_per_slice[s] residual tokens
+ *                      (a ragged batch); n_quant and res_count are then the
+ *                      upper bounds that size the work and the workspace,
+ *                      and the kernels clamp each value into [0, bound].  A
+ *                      slice with no token at all gets an all-zero output. */
 typedef struct kivi_attn_cache {
     const int32_t* k_codes;
     const void* k_scale;
@@ -332,6 +341,8 @@ typedef struct kivi_attn_cache {
     int64_t res_slots;
     int64_t res_head;
     int64_t res_count;
+    const int32_t* n_quant_per_slice;
+    const int32_t* res_count_per_slice;
 } kivi_attn_cache;
 
 /* Bytes of device workspace that kivi_decode_attention needs for these

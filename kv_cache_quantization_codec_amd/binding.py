@@ -55,7 +55,8 @@ class kivi_attn_cache(ctypes.Structure):
                 ("cap_tokens", ctypes.c_int64), ("n_quant", ctypes.c_int64),
                 ("res_k", ctypes.c_void_p), ("res_v", ctypes.c_void_p),
                 ("res_slice_stride", ctypes.c_int64), ("res_slots", ctypes.c_int64),
-                ("res_head", ctypes.c_int64), ("res_count", ctypes.c_int64)]
+                ("res_head", ctypes.c_int64), ("res_count", ctypes.c_int64),
+                ("n_quant_per_slice", ctypes.c_void_p), ("res_count_per_slice", ctypes.c_void_p)]
 
 
 # (name, restype, argtypes) of every symbol include/kivi.h declares
@@ -367,10 +368,17 @@ class AttnCache:
     slice (as from :func:`alloc_keys` / :func:`alloc_values`); ``n_quant`` of
     them are read.  ``res_k`` / ``res_v``: fp16 ``[S, slots, D]`` tensors (any
     slice stride) holding the residual as a ring whose oldest token is at
-    slot ``res_head``; ``res_count`` defaults to all slots."""
+    slot ``res_head``; ``res_count`` defaults to all slots.
+
+    Ragged batches: ``n_quant_per_slice`` / ``res_count_per_slice`` (int32
+    device tensors ``[S]``) give each slice its own counts, clamped to
+    ``[0, n_quant]`` / ``[0, res_count]``, which then act as upper bounds;
+    a slice with no token at all gets a zero output."""
 
     def __init__(self, cfg: Config, keys, values, n_quant: int, res_k=None, res_v=None,
-                 res_head: int = 0, res_count: int | None = None):
+                 res_head: int = 0, res_count: int | None = None,
+                 n_quant_per_slice: torch.Tensor | None = None,
+                 res_count_per_slice: torch.Tensor | None = None):
         D = cfg.head_dim
         vc, vs, vz = values
         kc, ks, kz = keys
@@ -387,11 +395,15 @@ class AttnCache:
                 raise ValueError("res_k and res_v must share slots and slice stride")
             stride, slots = res_k.stride(0), res_k.shape[1]
         count = slots if res_count is None else res_count
+        for t, nm in ((n_quant_per_slice, "n_quant_per_slice"), (res_count_per_slice, "res_count_per_slice")):
+            if t is not None and (t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous()
+                                  or t.shape[0] != kc.shape[0] or t.device.type != "cuda"):
+                raise ValueError(f"{nm}: expected contiguous int32 [n_slices] on the device")
         self.cfg = cfg
-        self._refs = (keys, values, res_k, res_v)
+        self._refs = (keys, values, res_k, res_v, n_quant_per_slice, res_count_per_slice)
         self.c = kivi_attn_cache(_ptr(kc), _ptr(ks), _ptr(kz), _ptr(vc), _ptr(vs), _ptr(vz),
                                  cap, n_quant, _ptr(res_k), _ptr(res_v), stride, slots,
-                                 res_head, count)
+                                 res_head, count, _ptr(n_quant_per_slice), _ptr(res_count_per_slice))
 
     @classmethod
     def from_stream(cls, st: Stream) -> "AttnCache":

@@ -402,6 +402,9 @@ int kivi_decode_attention(const kivi_config* cfg, const kivi_attn_cache* cache, 
     if (!__builtin_isfinite(sm_scale)) return KIVI_E_SHAPE;
     if (n_slices == 0) return KIVI_OK;
     if (c.n_quant + c.res_count < 1) return KIVI_E_SHAPE;
+    if ((c.n_quant_per_slice && (reinterpret_cast<uintptr_t>(c.n_quant_per_slice) & 3u)) ||
+        (c.res_count_per_slice && (reinterpret_cast<uintptr_t>(c.res_count_per_slice) & 3u)))
+        return KIVI_E_ALIGN;
     const kivi::AttnPlan plan = kivi::attn_plan(n_slices, c.n_quant, c.res_count);
     int64_t groups = 0;
     if (!mul_ok(n_slices, plan.n_splits, &groups) || groups > INT32_MAX) return KIVI_E_SHAPE;
@@ -439,6 +442,8 @@ int kivi_decode_attention(const kivi_config* cfg, const kivi_attn_cache* cache, 
     a.v_zero = static_cast<const uint16_t*>(c.v_zero);
     a.res_k = static_cast<const uint16_t*>(c.res_k);
     a.res_v = static_cast<const uint16_t*>(c.res_v);
+    a.n_quant_s = c.n_quant > 0 ? c.n_quant_per_slice : nullptr;
+    a.res_count_s = c.res_count > 0 ? c.res_count_per_slice : nullptr;
     a.q = static_cast<const uint16_t*>(q);
     a.out = static_cast<uint16_t*>(out);
     a.ws_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;

@@ -219,7 +219,9 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Acc<D>& ac
     const int r = a.q_per_kv;
     const int ha = 2 * kq, hb = 2 * kq + 1;
     if (a.plan.n_splits == 1) {
-        const float ia = 1.0f / acc.l_a, ib = 1.0f / acc.l_b;
+        // a slice with no token at all (ragged batch) has l = 0: output 0
+        const float ia = acc.l_a > 0.0f ? 1.0f / acc.l_a : 0.0f;
+        const float ib = acc.l_b > 0.0f ? 1.0f / acc.l_b : 0.0f;
 #pragma unroll
         for (int nt = 0; nt < D / 16; ++nt) {
             if (ha < r) a.out[(s * r + ha) * D + 16 * nt + j] = __builtin_bit_cast(uint16_t, (f16)(oa[nt] * ia));
@@ -262,6 +264,10 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     const int64_t s = blockIdx.x / a.plan.n_splits;
     const int split = (int)(blockIdx.x - s * a.plan.n_splits);
     const bool residual = a.plan.has_res && split == a.plan.n_splits - 1;
+    // this slice's token counts: uniform, or per slice (ragged) clamped to
+    // the bounds that sized the work
+    const int n_quant_s = a.n_quant_s ? min(max(a.n_quant_s[s], 0), a.n_quant) : a.n_quant;
+    const int res_count_s = a.res_count_s ? min(max(a.res_count_s[s], 0), a.res_count) : a.res_count;
 
     // operand rows that are never written stay zero
     for (int i = L; i < ROWS * (D + 8); i += kWave) (&sm.aq[0][0])[i] = (f16)0;
@@ -300,12 +306,12 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         // ---- fp16 residual: plain fp16 operands ----
         const uint16_t* rk = a.res_k + s * a.res_stride;
         const uint16_t* rv = a.res_v + s * a.res_stride;
-        for (int i0 = 0; i0 < a.res_count; i0 += 32) {
+        for (int i0 = 0; i0 < res_count_s; i0 += 32) {
             float xa[2], xb[2];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int i = i0 + 16 * tt + j;
-                const bool valid = i < a.res_count;
+                const bool valid = i < res_count_s;
                 int slot = a.res_head + (valid ? i : 0);
                 if (slot >= a.res_slots) slot -= a.res_slots;
                 const uint16_t* row = rk + (int64_t)slot * D;
@@ -330,7 +336,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = i0 + 8 * kq + e;
-                valid[e] = i < a.res_count;
+                valid[e] = i < res_count_s;
                 int slot = a.res_head + (valid[e] ? i : 0);
                 if (slot >= a.res_slots) slot -= a.res_slots;
                 vrow[e] = rv + (int64_t)slot * D + j;
@@ -358,8 +364,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
 
     // ---- quantized prefix: blocks [b0, b1) of 32 tokens ----
     const int b0 = split * a.plan.blocks_per_split;
-    const int b1 = min(b0 + a.plan.blocks_per_split, a.plan.n_blocks);
-    const int n = a.n_quant;
+    const int n = n_quant_s;
+    const int b1 = min(b0 + a.plan.blocks_per_split, (n + 31) / 32);
     constexpr int Wk = G * KB / 32;                       // key words per channel per group
     constexpr int NGV = (D + G - 1) / G;                  // value groups per row
     constexpr int WPT = NGV * G * VB / 32;                // value words per row
@@ -575,6 +581,12 @@ __global__ void __launch_bounds__(kWave) attention_merge_kernel(const AttnArgs a
     const int L = threadIdx.x;
     float mx = kNegInf;
     for (int i = 0; i < ns; ++i) mx = fmaxf(mx, a.ws_ml[((s * ns + i) * r + h) * 2]);
+    if (mx == kNegInf) {                       // a slice with no token at all: output 0
+        uint16_t* dst = a.out + (s * r + h) * D;
+        if (L < D) dst[L] = 0;
+        if (L + kWave < D) dst[L + kWave] = 0;
+        return;
+    }
     float lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int i = 0; i < ns; ++i) {
         const int64_t base = (s * ns + i) * r + h;
@@ -583,7 +595,7 @@ __global__ void __launch_bounds__(kWave) attention_merge_kernel(const AttnArgs a
         if (L < D) o0 += w * a.ws_o[base * D + L];
         if (L + kWave < D) o1 += w * a.ws_o[base * D + L + kWave];
     }
-    const float inv = 1.0f / lsum;
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;   // a slice with no token: 0
     uint16_t* dst = a.out + (s * r + h) * D;
     if (L < D) dst[L] = __builtin_bit_cast(uint16_t, (f16)(o0 * inv));
     if (L + kWave < D) dst[L + kWave] = __builtin_bit_cast(uint16_t, (f16)(o1 * inv));

@@ -115,6 +115,8 @@ struct AttnArgs {
     const uint16_t* v_zero;
     const uint16_t* res_k;    // fp16 residual rings
     const uint16_t* res_v;
+    const int32_t* n_quant_s; // per-slice counts (ragged batch) or nullptr
+    const int32_t* res_count_s;
     const uint16_t* q;        // fp16 [n_slices][q_per_kv][D]
     uint16_t* out;            // fp16 [n_slices][q_per_kv][D]
     float* ws_ml;             // [n_slices][n_splits][q_per_kv][2] (max, sum), when split

@@ -24,7 +24,7 @@ def _ws(c, S, r, nq, nres):
 def _cache(**over):
     f = dict(k_codes=FAKE, k_scale=FAKE, k_zero=FAKE, v_codes=FAKE, v_scale=FAKE, v_zero=FAKE,
              cap_tokens=256, n_quant=200, res_k=FAKE, res_v=FAKE, res_slice_stride=160 * 128,
-             res_slots=160, res_head=5, res_count=40)
+             res_slots=160, res_head=5, res_count=40, n_quant_per_slice=0, res_count_per_slice=0)
     f.update(over)
     return B.kivi_attn_cache(*(f[n] for n, _ in B.kivi_attn_cache._fields_))
 
@@ -89,6 +89,8 @@ def test_head_dim_limits(D, status):
     ({}, {"ws": FAKE + 4}, "KIVI_E_ALIGN"),
     ({"k_scale": FAKE + 2}, {}, "KIVI_E_ALIGN"),
     ({"res_k": FAKE + 8}, {}, "KIVI_E_ALIGN"),
+    ({"n_quant_per_slice": FAKE + 2}, {}, "KIVI_E_ALIGN"),
+    ({"res_count_per_slice": FAKE + 1}, {}, "KIVI_E_ALIGN"),
 ])
 def test_argument_errors(over, kw, status):
     c = _cfg()

@@ -267,3 +267,132 @@ def test_stream_cache_after_prefill_and_steps():
                  max(1, ws // (S * 2 * (D + 2) * 4)))
     got = out.cpu().numpy().astype(np.float64)
     assert np.all(np.abs(got - want) <= tol)
+
+
+# ragged batches ---------------------------------------------------------------
+
+def run_ragged(kb, vb, G, D, r, n_list, res_list, *, seed, cap=None, slots=None, head=0):
+    """Each slice i holds its own n_list[i] quantized tokens (encoded on their
+    own, so a partial last key group has its own statistics) and
+    res_list[i] residual tokens; the call passes the maxima as bounds plus
+    the per-slice counts.  Every slice is checked against the oracle over
+    its own cache; a slice with no token must give exactly 0."""
+    S = len(n_list)
+    n_max, res_max = max(n_list), max(res_list)
+    cap = max(n_max, 1) if cap is None else cap
+    slots = max(res_max, 1) if slots is None else slots
+    cfg = K.Config(kb, vb, G, 128, D)
+    k, v, q = _gen(seed, S, n_max, res_max, D, r)
+    rng = np.random.default_rng(seed + 1)
+    ngk_cap, Wk, Wv, ngv = -(-cap // G), G * kb // 32, G * vb // 32, -(-D // G)
+    kc = rng.integers(0, 2 ** 32, (S, ngk_cap * Wk, D), dtype=np.uint32)
+    ks = np.full((S, ngk_cap, D), NAN16, dtype=np.uint16)
+    kz = ks.copy()
+    vc = rng.integers(0, 2 ** 32, (S, cap, ngv * Wv), dtype=np.uint32)
+    vs = np.full((S, cap, ngv), NAN16, dtype=np.uint16)
+    vz = vs.copy()
+    rk = np.full((S, slots, D), NAN16, dtype=np.uint16)
+    rv = rk.copy()
+    per = []
+    for i, (n, nr) in enumerate(zip(n_list, res_list)):
+        kp = ref.encode_k(k[i:i + 1], n, kb, G) if n else None
+        vp = ref.encode_v(v[i:i + 1], n, vb, G) if n else None
+        if n:
+            ngk = -(-n // G)
+            kc[i, :ngk * Wk] = kp[0][0].view(np.uint32)
+            ks[i, :ngk], kz[i, :ngk] = kp[1][0].view(np.uint16), kp[2][0].view(np.uint16)
+            vc[i, :n] = vp[0][0].view(np.uint32)
+            vs[i, :n], vz[i, :n] = vp[1][0].view(np.uint16), vp[2][0].view(np.uint16)
+        res_k, res_v = k[i:i + 1, n_max:n_max + nr], v[i:i + 1, n_max:n_max + nr]
+        idx = (head + np.arange(nr)) % slots
+        rk[i, idx], rv[i, idx] = res_k[0].view(np.uint16), res_v[0].view(np.uint16)
+        per.append((kp, vp, n, res_k, res_v))
+    keys = (_to_dev(kc, torch.int32), _to_dev(ks.view(F16), torch.float16), _to_dev(kz.view(F16), torch.float16))
+    vals = (_to_dev(vc, torch.int32), _to_dev(vs.view(F16), torch.float16), _to_dev(vz.view(F16), torch.float16))
+    nq_s = torch.tensor(n_list, dtype=torch.int32, device="cuda")
+    nr_s = torch.tensor(res_list, dtype=torch.int32, device="cuda")
+    cache = K.AttnCache(cfg, keys, vals, n_max, _to_dev(rk.view(F16), torch.float16),
+                        _to_dev(rv.view(F16), torch.float16), head, res_max,
+                        n_quant_per_slice=nq_s, res_count_per_slice=nr_s)
+    qd = _to_dev(q, torch.float16)
+    out = torch.full_like(qd, float("nan"))
+    K.kivi_decode_attention(cfg, cache, qd, D ** -0.5, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ws = K.kivi_attention_workspace_bytes(cfg, S, r, n_max, res_max)
+    n_splits = max(1, ws // max(1, S * r * (D + 2) * 4))
+    for i, (kp, vp, n, res_k, res_v) in enumerate(per):
+        if n + res_k.shape[1] == 0:
+            assert np.array_equal(got[i], np.zeros_like(got[i])), f"slice {i}: empty cache must give 0"
+            continue
+        want = att.decode_attention(q[i:i + 1], kp, vp, n, res_k, res_v, kb, vb, G, D ** -0.5)
+        tol = _bound(q[i:i + 1], kp, vp, n, res_k, res_v, kb, vb, G, D ** -0.5, want, n_splits)
+        err = np.abs(got[i:i + 1] - want)
+        assert np.all(np.isfinite(got[i])), f"slice {i} (n={n}, res={res_k.shape[1]}): non-finite output"
+        assert np.all(err <= tol), (f"slice {i} (n={n}, res={res_k.shape[1]}): max err/tol "
+                                    f"{np.max(err / tol):.3g}")
+    return got
+
+
+def test_ragged_split_path():
+    # few slices and a long bound: the split plan and the merge kernel
+    run_ragged(2, 2, 32, 128, 4, [0, 1, 33, 700, 2000, 2047, 64, 0],
+               [0, 0, 5, 128, 0, 77, 128, 9], seed=21, slots=160, head=150)
+
+
+@pytest.mark.parametrize("part", ["quantized", "residual"])
+def test_ragged_single_pass(part):
+    # at most 4 blocks and no residual, or a residual only: one workgroup
+    # per slice writes the output directly (no merge)
+    counts = [(37 * i) % 129 for i in range(96)]
+    counts[5] = 0
+    zeros = [0] * 96
+    n_list, res_list = (counts, zeros) if part == "quantized" else (zeros, counts)
+    cfg = K.Config(4, 2, 64, 128, 128)
+    assert K.kivi_attention_workspace_bytes(cfg, 96, 1, max(n_list), max(res_list)) == 0
+    run_ragged(4, 2, 64, 128, 1, n_list, res_list, seed=22)
+
+
+@pytest.mark.parametrize("kb,vb,G,D,r", [(8, 4, 128, 128, 8), (2, 8, 32, 64, 2), (4, 4, 64, 96, 3)])
+def test_ragged_formats(kb, vb, G, D, r):
+    run_ragged(kb, vb, G, D, r, [300, 0, 129, 1], [3, 40, 0, 1], seed=kb + vb + G, cap=384)
+
+
+def test_ragged_counts_are_clamped_to_the_bounds():
+    """Per-slice counts above the bounds (or negative) act as the bounds
+    (or 0): the same output as the clamped counts."""
+    cfg = K.Config(2, 2, 32, 128, 64)
+    S, n, nr, D = 3, 200, 20, 64
+    k, v, q = _gen(31, S, n, nr, D, 1)
+    keys, vals = _payload_dev(ref.encode_k(k, n, 2, 32), ref.encode_v(v, n, 2, 32), n, n, 32, D, 2, 2)
+    rk, rv = _ring_dev(k[:, n:], v[:, n:], nr, 0)
+    outs = []
+    for nq_l, nr_l in (([n, 10 ** 6, -5], [nr, 999, -1]), ([n, n, 0], [nr, nr, 0])):
+        cache = K.AttnCache(cfg, keys, vals, n, rk, rv, 0, nr,
+                            n_quant_per_slice=torch.tensor(nq_l, dtype=torch.int32, device="cuda"),
+                            res_count_per_slice=torch.tensor(nr_l, dtype=torch.int32, device="cuda"))
+        out = torch.full((S, 1, D), float("nan"), dtype=torch.float16, device="cuda")
+        K.kivi_decode_attention(cfg, cache, _to_dev(q, torch.float16), D ** -0.5, out)
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
+    assert torch.count_nonzero(outs[0][2]) == 0
+
+
+def test_ragged_uniform_counts_equal_the_uniform_call_bitwise():
+    cfg = K.Config(2, 4, 32, 128, 128)
+    S, n, nr, D = 4, 900, 60, 128
+    k, v, q = _gen(41, S, n, nr, D, 2)
+    keys, vals = _payload_dev(ref.encode_k(k, n, 2, 32), ref.encode_v(v, n, 4, 32), n, n, 32, D, 2, 4)
+    rk, rv = _ring_dev(k[:, n:], v[:, n:], nr, 0)
+    qd = _to_dev(q, torch.float16)
+    outs = []
+    for per in (False, True):
+        kw = {}
+        if per:
+            kw = dict(n_quant_per_slice=torch.full((S,), n, dtype=torch.int32, device="cuda"),
+                      res_count_per_slice=torch.full((S,), nr, dtype=torch.int32, device="cuda"))
+        cache = K.AttnCache(cfg, keys, vals, n, rk, rv, 0, nr, **kw)
+        out = torch.empty_like(qd)
+        K.kivi_decode_attention(cfg, cache, qd, D ** -0.5, out)
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
