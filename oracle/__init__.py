@@ -14,6 +14,8 @@ Two tiers, written independently of each other and of the HIP path:
   token per head over the dequantized prefix plus the fp16 residual.
 * :mod:`oracle.fp8_ref` -- FP8 (E4M3) keys of the k8v4 layout, by nearest
   value over the listed code points.
+* :mod:`oracle.layer_mix_ref` -- per-layer bit mixes: the protected boundary
+  layers of a model, and layer-by-layer coding of a mixed cache.
 
 Sources (titles of the pages the method is taken from):
 
@@ -34,4 +36,4 @@ The pages print no formula for the statistics or the rounding; the readings
 used here are stated in each function's docstring.
 """
 
-from . import attention_ref, fp8_ref, kivi_exact, kivi_ref  # noqa: F401
+from . import attention_ref, fp8_ref, kivi_exact, kivi_ref, layer_mix_ref  # noqa: F401
