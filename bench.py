@@ -244,39 +244,48 @@ def attention_cpu_baseline(w, k, v, kq, vq, q, n, sm_scale, alg, budget_s):
 
 def cpu_baseline(k, v, w, cfg, n, budget_s=12.0):
     """Time the numpy oracle (single thread) on whole slices of the same cache
-    until about ``budget_s`` seconds of CPU work; scale to fp16-eq GB/s."""
-    import numpy as np
-
-    from oracle import kivi_ref as ref
-
+    until about ``budget_s`` seconds of CPU work; scale to fp16-eq GB/s.
+    Chunks of 8 slices are taken from the layers in turn, each coded with
+    its layer's bits (the oracle's boundary rule for a per-layer mix)."""
     from oracle import fp8_ref as f8
+    from oracle import kivi_ref as ref
+    from oracle import layer_mix_ref as mix
 
     G = cfg.group_size
+    spl = w.slices_per_layer
+    bits = mix.layer_bits(w.layers, w.boundary, (cfg.k_bits, cfg.v_bits), w.boundary_bits)
     done = 0
     spent = 0.0
     S = k.shape[0]
     chunk = 8
+    c = 0
     while spent < budget_s and done < S:
-        sl = slice(done, min(done + chunk, S))
+        layer, off = c % w.layers, (c // w.layers) * chunk
+        c += 1
+        if off >= spl:
+            break
+        sl = slice(layer * spl + off, layer * spl + min(off + chunk, spl))
+        kb, vb = bits[layer]
         kh = k[sl].cpu().numpy()
         vh = v[sl].cpu().numpy()
         t0 = time.perf_counter()
         if w.fp8_keys:
             f8.decode(f8.encode_keys(kh, n))
         else:
-            kc, ks, kz = ref.encode_k(kh, n, cfg.k_bits, G)
-            ref.decode_k(kc, ks, kz, n, cfg.k_bits, G)
-        vc, vs, vz = ref.encode_v(vh, n, cfg.v_bits, G)
-        ref.decode_v(vc, vs, vz, n, cfg.v_bits, G, cfg.head_dim)
+            kc, ks, kz = ref.encode_k(kh, n, kb, G)
+            ref.decode_k(kc, ks, kz, n, kb, G)
+        vc, vs, vz = ref.encode_v(vh, n, vb, G)
+        ref.decode_v(vc, vs, vz, n, vb, G, cfg.head_dim)
         spent += time.perf_counter() - t0
-        done = sl.stop
+        done += sl.stop - sl.start
     fp16_bytes = 2 * 2 * done * n * cfg.head_dim * 2
     return {
         "value": round(fp16_bytes / spent / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{done} of {S} slices ({done * n} tokens x {cfg.head_dim} channels, K and V), "
+        "sample": f"{done} of {S} slices, {chunk} at a time from the layers in turn "
+                  f"({done * n} tokens x {cfg.head_dim} channels, K and V), "
                   f"numpy oracle encode+decode, {spent:.1f} s single-threaded "
                   f"(host has {len(os.sched_getaffinity(0))} cores available)",
     }
@@ -456,7 +465,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama2_7b_2bit",
                     choices=["llama2_7b_2bit", "mistral_7b_k2v4", "single_layer_4bit",
-                             "llama2_7b_k8v4", "stream_b64"])
+                             "llama2_7b_k8v4", "llama2_7b_mix", "stream_b64"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-ceiling", action="store_true",
@@ -502,10 +511,31 @@ def main():
         k[layer * spl:(layer + 1) * spl] = kl
         v[layer * spl:(layer + 1) * spl] = vl
         del kl, vl
-    vq = K.alloc_values(cfg, S, n, dev)
     ko = torch.empty((S, n, D), dtype=torch.float16, device=dev)
     vo = torch.empty_like(ko)
     names = ["encode_k", "encode_v", "decode_k", "decode_v"]
+    launches = {nm: 1 for nm in names}
+    if w.boundary:
+        # per-layer bit mix: the library's boundary rule, one config per layer,
+        # each run of equal layers in one allocation (one launch per run)
+        prot = set(K.kivi_boundary_layers(w.layers, w.boundary))
+        cfgs = [K.Config(*(w.boundary_bits if l in prot else (w.k_bits, w.v_bits)), G,
+                         w.residual_length, D) for l in range(w.layers)]
+        kl_ = K.alloc_layers(cfgs, spl, n, dev, keys=True)
+        vl_ = K.alloc_layers(cfgs, spl, n, dev, keys=False)
+        k4, v4 = k.view(w.layers, spl, T, D), v.view(w.layers, spl, T, D)
+        ko4, vo4 = ko.view(w.layers, spl, n, D), vo.view(w.layers, spl, n, D)
+        calls = [
+            lambda: K.kivi_encode_k_layers(cfgs, k4, n, kl_),
+            lambda: K.kivi_encode_v_layers(cfgs, v4, n, vl_),
+            lambda: K.kivi_decode_k_layers(cfgs, kl_, n, ko4),
+            lambda: K.kivi_decode_v_layers(cfgs, vl_, n, vo4),
+        ]
+        for nm, keys in (("encode_k", True), ("encode_v", False), ("decode_k", True), ("decode_v", False)):
+            sides = [(c.k_bits if keys else c.v_bits) for c in cfgs]
+            launches[nm] = 1 + sum(1 for a, b in zip(sides, sides[1:]) if a != b)
+    else:
+        vq = K.alloc_values(cfg, S, n, dev)
     if w.fp8_keys:
         kq = torch.empty((S, n, D), dtype=torch.uint8, device=dev)
         calls = [
@@ -514,7 +544,7 @@ def main():
             lambda: K.kivi_fp8_decode(kq, n, ko),
             lambda: K.kivi_decode_v(cfg, *vq, n, vo),
         ]
-    else:
+    elif not w.boundary:
         kq = K.alloc_keys(cfg, S, n, dev)
         calls = [
             lambda: K.kivi_encode_k(cfg, k, n, *kq),
@@ -545,6 +575,10 @@ def main():
     fp16_eq = 2 * 2 * S * n * D * 2                  # K and V, encode + decode
     bits = {"encode_k": w.k_bits, "decode_k": w.k_bits, "encode_v": w.v_bits, "decode_v": w.v_bits}
     alg = {nm: algorithmic_bytes(nm[-1], nm[:6], S, n, D, G, bits[nm]) for nm in names}
+    if w.boundary:                                    # each layer at its own bits
+        alg = {nm: sum(algorithmic_bytes(nm[-1], nm[:6], spl, n, D, G,
+                                         c.k_bits if nm[-1] == "k" else c.v_bits) for c in cfgs)
+               for nm in names}
     if w.fp8_keys:                                    # 2 bytes in, 1 out (and back)
         alg["encode_k"] = alg["decode_k"] = 3 * S * n * D
     moved = sum(alg.values())
@@ -572,6 +606,7 @@ def main():
             "seq_len": T, "quantized_tokens": n, "residual_length": w.residual_length,
             "k_bits": w.k_bits, "v_bits": w.v_bits, "group_size": G,
             "key_format": "fp8_e4m3" if w.fp8_keys else "kivi",
+            **({"boundary_layers": sorted(prot), "boundary_bits": list(w.boundary_bits)} if w.boundary else {}),
         },
         "moved_GBps": round(moved / (ms_step / 1000.0) / 1e9, 2),
         "hbm_roofline_frac_step": round(moved / (ms_step / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -586,10 +621,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": alg[dom],
+            "algorithmic_bytes_per_launch": alg[dom] // launches[dom],
+            **({"launches_per_call": launches[dom]} if launches[dom] > 1 else {}),
         },
     }
-    if not w.fp8_keys:
+    if not w.fp8_keys and not w.boundary:
         out["attention"] = attention_bench(w, cfg, k, v, kq, vq, n, args, dev)
     if args.copy_ceiling:
         out["copy_ceiling_GBps"] = copy_ceiling(dev)

@@ -166,6 +166,57 @@ int kivi_decode_v(const kivi_config* cfg, const int32_t* codes,
                   int64_t n_slices, int64_t n_tokens, int64_t cap_tokens,
                   void* out_fp16, int64_t out_slice_stride, void* hip_stream);
 
+/* Per-layer bit mixes (vLLM turboquant/config.py, get_boundary_skip_layers:
+ * "boundary protection" exempts the first n and the last n attention
+ * layers of a dense model from an aggressive preset; n is capped at half the
+ * layer count and the two sets are merged).  Here a protected layer takes a
+ * configuration of its own (normally more bits) instead of no compression;
+ * keeping those layers in fp16 is the caller's choice of not coding them.
+ *
+ * kivi_boundary_layers: for a model of n_layers layers, sets flags[l] = 1
+ * for the protected layers and 0 for the others (flags: host int32
+ * [n_layers]).  Returns the number of protected layers (>= 0),
+ * KIVI_E_SHAPE for n_layers < 0, KIVI_E_NULL for flags == NULL with
+ * n_layers > 0.  n <= 0 protects nothing.  Host only. */
+int kivi_boundary_layers(int64_t n_layers, int64_t n, int32_t* flags);
+
+/* Coding of a model cache whose layers may have different configurations.
+ * cfgs: host array of n_layers configurations (all with one head_dim).
+ * Every layer has n_slices slices and a capacity of cap_tokens tokens.
+ * fp16 side: layer l starts at element l*layer_stride of the input (encode)
+ * or output (decode) array, and within a layer the layout is the
+ * single-layer one with slice_stride; layer_stride >= n_slices*slice_stride,
+ * a multiple of 8.  Payload side: codes[l], scale[l], zero[l] are host
+ * arrays of n_layers device pointers, layer l's key (or value) layouts, as
+ * for the single-layer calls.
+ * Results are those of one single-layer call per layer with cfgs[l].  A
+ * run of consecutive layers is coded by ONE launch over all its slices when
+ * the layers agree on the coded side's bits, group_size and head_dim, the
+ * fp16 layers are back to back (layer_stride == n_slices*slice_stride) and
+ * each payload array of a layer starts where the previous layer's ends
+ * (which is how a caller lays out a mix in one allocation per run); other
+ * layers get a launch each.  The 16-byte alignment rule applies to the
+ * arrays of each run's first layer only: the other layers of a run are
+ * addressed as slices of those arrays.  Every layer's arguments are checked
+ * before the first launch, so an error other than KIVI_E_HIP enqueues
+ * nothing. */
+int kivi_encode_k_layers(const kivi_config* cfgs, int64_t n_layers, const void* k_fp16,
+                         int64_t layer_stride, int64_t n_slices, int64_t n_tokens,
+                         int64_t slice_stride, int64_t cap_tokens, int32_t* const* codes,
+                         void* const* scale_fp16, void* const* zero_fp16, void* hip_stream);
+int kivi_encode_v_layers(const kivi_config* cfgs, int64_t n_layers, const void* v_fp16,
+                         int64_t layer_stride, int64_t n_slices, int64_t n_tokens,
+                         int64_t slice_stride, int64_t cap_tokens, int32_t* const* codes,
+                         void* const* scale_fp16, void* const* zero_fp16, void* hip_stream);
+int kivi_decode_k_layers(const kivi_config* cfgs, int64_t n_layers, const int32_t* const* codes,
+                         const void* const* scale_fp16, const void* const* zero_fp16,
+                         int64_t n_slices, int64_t n_tokens, int64_t cap_tokens, void* out_fp16,
+                         int64_t layer_stride, int64_t slice_stride, void* hip_stream);
+int kivi_decode_v_layers(const kivi_config* cfgs, int64_t n_layers, const int32_t* const* codes,
+                         const void* const* scale_fp16, const void* const* zero_fp16,
+                         int64_t n_slices, int64_t n_tokens, int64_t cap_tokens, void* out_fp16,
+                         int64_t layer_stride, int64_t slice_stride, void* hip_stream);
+
 /* Streaming state of the decode phase (CacheForge README, "How it works"
  * and its figure on the quantization flow during prefill and decoding: the
  * recent tokens stay fp16 while older ones are quantized).  Device arrays:

@@ -11,14 +11,20 @@ from .binding import (  # noqa: E402,F401
     KiviError,
     Stream,
     alloc_keys,
+    alloc_layers,
     alloc_values,
     kivi_append_flush,
     kivi_attention_workspace_bytes,
+    kivi_boundary_layers,
     kivi_decode_attention,
     kivi_decode_k,
+    kivi_decode_k_layers,
     kivi_decode_v,
+    kivi_decode_v_layers,
     kivi_encode_k,
+    kivi_encode_k_layers,
     kivi_encode_v,
+    kivi_encode_v_layers,
     kivi_fp8_decode,
     kivi_fp8_encode,
     kivi_k_code_words,

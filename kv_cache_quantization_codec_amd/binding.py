@@ -77,6 +77,11 @@ SIGNATURES = [
     ("kivi_encode_v", _I32, [_CFG, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
     ("kivi_decode_k", _I32, [_CFG, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     ("kivi_decode_v", _I32, [_CFG, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
+    ("kivi_boundary_layers", _I32, [_I64, _I64, _P]),
+    ("kivi_encode_k_layers", _I32, [_CFG, _I64, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
+    ("kivi_encode_v_layers", _I32, [_CFG, _I64, _P, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P]),
+    ("kivi_decode_k_layers", _I32, [_CFG, _I64, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _I64, _P]),
+    ("kivi_decode_v_layers", _I32, [_CFG, _I64, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _I64, _P]),
     ("kivi_stream_prefill", _I32, [_CFG, _ST, _P, _P, _I64, _I64, _P]),
     ("kivi_append_flush", _I32, [_CFG, _ST, _P, _P, _P]),
     ("kivi_fp8_encode", _I32, [_P, _I64, _I64, _I64, _I64, _P, _I64, _P]),
@@ -233,6 +238,103 @@ def kivi_decode_v(cfg, codes, scale, zero, n_tokens: int, out: torch.Tensor,
     cap = n_tokens if cap_tokens is None else cap_tokens
     _check(lib().kivi_decode_v(_cfg(cfg), _ptr(codes), _ptr(scale), _ptr(zero), S, n_tokens, cap,
                                _ptr(out), stride, _stream_ptr(stream)), "kivi_decode_v")
+
+
+# ---------------------------------------------------------------------------
+# per-layer bit mixes
+# ---------------------------------------------------------------------------
+
+def kivi_boundary_layers(n_layers: int, n: int) -> list[int]:
+    """Indices of the protected (boundary) layers of an ``n_layers`` model."""
+    flags = (ctypes.c_int32 * max(n_layers, 1))()
+    count = lib().kivi_boundary_layers(n_layers, n, flags)
+    if count < 0:
+        raise KiviError(count, "kivi_boundary_layers")
+    return [l for l in range(n_layers) if flags[l]]
+
+
+def _side(c: Config, keys: bool):
+    return (c.k_bits if keys else c.v_bits, c.group_size, c.head_dim)
+
+
+def alloc_layers(cfgs, n_slices: int, cap_tokens: int, device="cuda", keys: bool = True):
+    """Per-layer key (or value) payloads for a model whose layer l uses
+    ``cfgs[l]``.  Consecutive layers with the same configuration on that side
+    share one allocation, back to back, so the ``*_layers`` calls code each
+    such run with one launch.  Returns a list of (codes, scale, zero) views."""
+    out, l = [], 0
+    alloc = alloc_keys if keys else alloc_values
+    while l < len(cfgs):
+        m = l + 1
+        while m < len(cfgs) and _side(cfgs[m], keys) == _side(cfgs[l], keys):
+            m += 1
+        codes, scale, zero = alloc(cfgs[l], n_slices * (m - l), cap_tokens, device)
+        for i in range(m - l):
+            sl = slice(i * n_slices, (i + 1) * n_slices)
+            out.append((codes[sl], scale[sl], zero[sl]))
+        l = m
+    return out
+
+
+def _cfg_array(cfgs):
+    return (kivi_config * max(len(cfgs), 1))(*[c.c() if isinstance(c, Config) else c for c in cfgs])
+
+
+def _fp16_layers(t: torch.Tensor, D: int, what: str):
+    """(n_layers, n_slices, layer_stride, slice_stride) of an fp16 [L, S, T, D]
+    tensor with contiguous token rows."""
+    if t.dtype != torch.float16 or t.dim() != 4 or t.shape[3] != D:
+        raise ValueError(f"{what}: expected float16 [L, S, T, {D}], got {t.dtype} {tuple(t.shape)}")
+    if t.stride(3) != 1 or (t.shape[2] > 1 and t.stride(2) != D):
+        raise ValueError(f"{what}: tokens must be contiguous rows of {D} elements")
+    return t.shape[0], t.shape[1], t.stride(0), t.stride(1)
+
+
+def _layer_ptrs(layers, L: int):
+    if len(layers) != L:
+        raise ValueError(f"expected {L} per-layer payloads, got {len(layers)}")
+    arrs = [(ctypes.c_void_p * max(L, 1))(*[_ptr(p[i]) for p in layers]) for i in range(3)]
+    return arrs
+
+
+def _coded_layers(name: str, keys: bool, cfgs, x: torch.Tensor, n_tokens: int, layers, cap_tokens,
+                  stream):
+    L, S, lstride, sstride = _fp16_layers(x, cfgs[0].head_dim if cfgs else 0, "k" if keys else "v")
+    if len(cfgs) != L:
+        raise ValueError(f"expected {L} configurations, got {len(cfgs)}")
+    cap = n_tokens if cap_tokens is None else cap_tokens
+    codes, scale, zero = _layer_ptrs(layers, L)
+    fn = getattr(lib(), name)
+    if name.startswith("kivi_encode"):
+        st = fn(_cfg_array(cfgs), L, _ptr(x), lstride, S, n_tokens, sstride, cap, codes, scale, zero,
+                _stream_ptr(stream))
+    else:
+        st = fn(_cfg_array(cfgs), L, codes, scale, zero, S, n_tokens, cap, _ptr(x), lstride, sstride,
+                _stream_ptr(stream))
+    _check(st, name)
+
+
+def kivi_encode_k_layers(cfgs, k: torch.Tensor, n_tokens: int, layers, cap_tokens: int | None = None,
+                         stream=None):
+    """Keys ``k`` fp16 [L, S, T, D]: layer l coded with ``cfgs[l]`` into
+    ``layers[l]`` = (codes, scale, zero)."""
+    _coded_layers("kivi_encode_k_layers", True, cfgs, k, n_tokens, layers, cap_tokens, stream)
+
+
+def kivi_encode_v_layers(cfgs, v: torch.Tensor, n_tokens: int, layers, cap_tokens: int | None = None,
+                         stream=None):
+    _coded_layers("kivi_encode_v_layers", False, cfgs, v, n_tokens, layers, cap_tokens, stream)
+
+
+def kivi_decode_k_layers(cfgs, layers, n_tokens: int, out: torch.Tensor, cap_tokens: int | None = None,
+                         stream=None):
+    """Dequantize every layer's key tokens [0, n_tokens) into ``out`` fp16 [L, S, >=n_tokens, D]."""
+    _coded_layers("kivi_decode_k_layers", True, cfgs, out, n_tokens, layers, cap_tokens, stream)
+
+
+def kivi_decode_v_layers(cfgs, layers, n_tokens: int, out: torch.Tensor, cap_tokens: int | None = None,
+                         stream=None):
+    _coded_layers("kivi_decode_v_layers", False, cfgs, out, n_tokens, layers, cap_tokens, stream)
 
 
 # ---------------------------------------------------------------------------

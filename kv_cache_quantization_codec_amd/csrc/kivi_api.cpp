@@ -213,6 +213,83 @@ int64_t attention_ws_bytes(const kivi_config* c, int64_t n_slices, int32_t q_per
     return total;
 }
 
+// ---- layer-wise coding of a model with per-layer configurations ----
+
+uintptr_t addr(const void* p) { return reinterpret_cast<uintptr_t>(p); }
+
+// A host array of device pointers of any pointee type, read as void pointers.
+const void* const* cv(const void* p) { return static_cast<const void* const*>(p); }
+
+// Layers a and b can share one launch on this side of the codec.
+bool same_side(const kivi_config& a, const kivi_config& b, bool keys) {
+    return a.group_size == b.group_size && a.head_dim == b.head_dim &&
+           (keys ? a.k_bits == b.k_bits : a.v_bits == b.v_bits);
+}
+
+// Bytes of one layer's codes and of one of its sidecars.
+void layer_bytes(const kivi_config& c, bool keys, int64_t n_slices, int64_t cap, int64_t* code_b,
+                 int64_t* stat_b) {
+    *code_b = 4 * n_slices * (keys ? k_words(&c, cap) : v_words(&c, cap));
+    *stat_b = 2 * n_slices * (keys ? k_stats(&c, cap) : v_stats(&c, cap));
+}
+
+// Checks every layer, then calls run(first, count) once per run of layers
+// that one launch can code (same side configuration, fp16 layers and
+// payload arrays back to back).  run is the single-layer entry point over
+// count*n_slices slices.
+template <class Run>
+int coded_layers(bool keys, const kivi_config* cfgs, int64_t n_layers, const void* fp16,
+                 int64_t layer_stride, int64_t n_slices, int64_t n_tokens, int64_t slice_stride,
+                 int64_t cap, const void* const* codes, const void* const* scale,
+                 const void* const* zero, Run run) {
+    if (n_layers < 0) return KIVI_E_SHAPE;
+    if (n_layers == 0) return KIVI_OK;
+    if (!cfgs) return KIVI_E_NULL;
+    for (int64_t l = 0; l < n_layers; ++l) {
+        const int st = check_config(&cfgs[l]);
+        if (st) return st;
+        if (cfgs[l].head_dim != cfgs[0].head_dim) return KIVI_E_HEAD_DIM;
+    }
+    if (n_slices == 0 || n_tokens == 0) return (n_slices < 0 || n_tokens < 0) ? KIVI_E_SHAPE : KIVI_OK;
+    for (int64_t l = 0; l < n_layers; ++l) {
+        const int st = check_common(&cfgs[l], n_slices, n_tokens, cap, slice_stride, keys);
+        if (st) return st;
+    }
+    int64_t layer_min = 0, span = 0;
+    if (layer_stride % 8 != 0) return KIVI_E_ALIGN;
+    if (!mul_ok(n_slices, slice_stride, &layer_min) || layer_stride < layer_min) return KIVI_E_SHAPE;
+    if (!mul_ok(n_layers - 1, layer_stride, &span) || __builtin_add_overflow(span, layer_min, &span) ||
+        !mul_ok(span, 2, &span))
+        return KIVI_E_SHAPE;
+    if (!fp16 || !codes || !scale || !zero) return KIVI_E_NULL;
+    if (!aligned16(fp16)) return KIVI_E_ALIGN;
+    for (int64_t l = 0; l < n_layers; ++l)
+        if (!codes[l] || !scale[l] || !zero[l]) return KIVI_E_NULL;
+    // end of the run that starts at layer a
+    const bool fp16_packed = layer_stride == layer_min;
+    auto run_end = [&](int64_t a) {
+        int64_t b = a + 1, code_b = 0, stat_b = 0;
+        layer_bytes(cfgs[a], keys, n_slices, cap, &code_b, &stat_b);
+        while (b < n_layers && fp16_packed && same_side(cfgs[b], cfgs[a], keys) &&
+               addr(codes[b]) == addr(codes[b - 1]) + code_b &&
+               addr(scale[b]) == addr(scale[b - 1]) + stat_b &&
+               addr(zero[b]) == addr(zero[b - 1]) + stat_b)
+            ++b;
+        return b;
+    };
+    // only a run's first layer needs aligned arrays: the launch addresses the
+    // others from it, as slices of one array
+    for (int64_t a = 0; a < n_layers; a = run_end(a))
+        if (!aligned16(codes[a]) || !aligned16(scale[a]) || !aligned16(zero[a])) return KIVI_E_ALIGN;
+    for (int64_t a = 0; a < n_layers;) {
+        const int64_t b = run_end(a);
+        const int st = run(a, b - a);
+        if (st) return st;
+        a = b;
+    }
+    return KIVI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -276,6 +353,65 @@ int kivi_decode_v(const kivi_config* cfg, const int32_t* codes, const void* scal
                   int64_t n_slices, int64_t n_tokens, int64_t cap, void* out, int64_t out_stride,
                   void* stream) {
     return decode(false, cfg, codes, scale, zero, n_slices, n_tokens, cap, out, out_stride, stream);
+}
+
+int kivi_boundary_layers(int64_t n_layers, int64_t n, int32_t* flags) {
+    if (n_layers < 0) return KIVI_E_SHAPE;
+    if (n_layers == 0) return 0;
+    if (!flags) return KIVI_E_NULL;
+    const int64_t m = n <= 0 ? 0 : (n < n_layers / 2 ? n : n_layers / 2);
+    int count = 0;
+    for (int64_t l = 0; l < n_layers; ++l) {
+        flags[l] = (l < m || n_layers - 1 - l < m) ? 1 : 0;
+        count += flags[l];
+    }
+    return count;
+}
+
+int kivi_encode_k_layers(const kivi_config* cfgs, int64_t n_layers, const void* k, int64_t layer_stride,
+                         int64_t n_slices, int64_t n_tokens, int64_t slice_stride, int64_t cap,
+                         int32_t* const* codes, void* const* scale, void* const* zero, void* stream) {
+    return coded_layers(true, cfgs, n_layers, k, layer_stride, n_slices, n_tokens, slice_stride, cap,
+                        cv(codes), cv(scale), cv(zero), [&](int64_t a, int64_t count) {
+                            return encode(true, &cfgs[a], static_cast<const uint16_t*>(k) + a * layer_stride,
+                                          count * n_slices, n_tokens, slice_stride, cap, codes[a],
+                                          scale[a], zero[a], stream);
+                        });
+}
+
+int kivi_encode_v_layers(const kivi_config* cfgs, int64_t n_layers, const void* v, int64_t layer_stride,
+                         int64_t n_slices, int64_t n_tokens, int64_t slice_stride, int64_t cap,
+                         int32_t* const* codes, void* const* scale, void* const* zero, void* stream) {
+    return coded_layers(false, cfgs, n_layers, v, layer_stride, n_slices, n_tokens, slice_stride, cap,
+                        cv(codes), cv(scale), cv(zero), [&](int64_t a, int64_t count) {
+                            return encode(false, &cfgs[a], static_cast<const uint16_t*>(v) + a * layer_stride,
+                                          count * n_slices, n_tokens, slice_stride, cap, codes[a],
+                                          scale[a], zero[a], stream);
+                        });
+}
+
+int kivi_decode_k_layers(const kivi_config* cfgs, int64_t n_layers, const int32_t* const* codes,
+                         const void* const* scale, const void* const* zero, int64_t n_slices,
+                         int64_t n_tokens, int64_t cap, void* out, int64_t layer_stride,
+                         int64_t slice_stride, void* stream) {
+    return coded_layers(true, cfgs, n_layers, out, layer_stride, n_slices, n_tokens, slice_stride, cap,
+                        cv(codes), scale, zero, [&](int64_t a, int64_t count) {
+                            return decode(true, &cfgs[a], codes[a], scale[a], zero[a], count * n_slices,
+                                          n_tokens, cap, static_cast<uint16_t*>(out) + a * layer_stride,
+                                          slice_stride, stream);
+                        });
+}
+
+int kivi_decode_v_layers(const kivi_config* cfgs, int64_t n_layers, const int32_t* const* codes,
+                         const void* const* scale, const void* const* zero, int64_t n_slices,
+                         int64_t n_tokens, int64_t cap, void* out, int64_t layer_stride,
+                         int64_t slice_stride, void* stream) {
+    return coded_layers(false, cfgs, n_layers, out, layer_stride, n_slices, n_tokens, slice_stride, cap,
+                        cv(codes), scale, zero, [&](int64_t a, int64_t count) {
+                            return decode(false, &cfgs[a], codes[a], scale[a], zero[a], count * n_slices,
+                                          n_tokens, cap, static_cast<uint16_t*>(out) + a * layer_stride,
+                                          slice_stride, stream);
+                        });
 }
 
 int kivi_stream_prefill(const kivi_config* cfg, kivi_stream* st, const void* k, const void* v,

@@ -41,6 +41,8 @@ class Workload:
     steps: int = 0          # streaming decode steps (0 = full-cache encode)
     q_per_kv: int = 1       # query heads per KV head at decode (grouped-query attention)
     fp8_keys: bool = False  # k8v4 layout: FP8 keys, values with one group per head
+    boundary: int = 0       # first and last `boundary` layers take `boundary_bits` (per-layer mix)
+    boundary_bits: tuple = (8, 8)
 
     @property
     def slices_per_layer(self) -> int:
@@ -60,6 +62,9 @@ WORKLOADS = {
                                 32, 16, 8, 16384, 128, 2, 4, 32, 128, q_per_kv=4),
     "llama2_7b_k8v4": Workload(5, "Llama-2-7B-shaped cache, batch 8, 4096 tokens, FP8 keys + 4-bit values",
                                32, 8, 32, 4096, 128, 8, 4, 128, 128, fp8_keys=True),
+    "llama2_7b_mix": Workload(6, "Llama-2-7B-shaped cache, batch 8, 4096 tokens, 2/2-bit with the first "
+                                 "and last 2 layers at 8/8-bit", 32, 8, 32, 4096, 128, 2, 2, 32, 128,
+                              boundary=2, boundary_bits=(8, 8)),
     "stream_b64": Workload(4, "streaming decode, batch 64, prefill 2048 + 512 steps, 2/2-bit",
                            32, 64, 8, 2048, 128, 2, 2, 32, 128, steps=512),
 }
@@ -128,7 +133,7 @@ def layer_kv(w: Workload, layer: int, device="cpu", tokens: int | None = None):
         v = _normal(shape, gv, device)
         if w.number == 1:
             k *= _single_layer_key_outliers(w, D).to(device)[None, :, None, :]
-        elif w.number == 2:
+        elif w.number in (2, 6):
             k *= _bernoulli_key_outliers(w, layer, D).to(device)[None, :, None, :]
     k = k.to(torch.float16).reshape(w.batch * w.heads, T, D)
     v = v.to(torch.float16).reshape(w.batch * w.heads, T, D)
