@@ -131,22 +131,27 @@ __device__ __forceinline__ void split_hl(float x, f16& hi, f16& lo) {
 }
 
 // LDS of one wave (D = head_dim, at most RMAX query heads per KV slice, so
-// 2*RMAX live MFMA rows; lanes of the other rows use zero operands without
-// reading LDS).  Row strides are padded by 16 bytes so that the rows an
-// MFMA operand read touches fall in different banks.  Sizing the rows by
-// RMAX keeps the multi-head case small enough for LDS not to limit the
-// number of resident waves.
+// 2*RMAX live MFMA rows).  When that leaves MFMA rows dead (2*RMAX < 16),
+// each A-operand array has one more row that is always zero: lanes of the
+// dead rows read it (one address, a broadcast), so operand reads need no
+// exec masking.  Row strides are padded
+// by 16 bytes so that the rows an MFMA operand read touches fall in
+// different banks.  Sizing the rows by RMAX keeps the multi-head case small
+// enough for LDS not to limit the number of resident waves.
+template <int RMAX>
+constexpr int operand_rows() { return 2 * RMAX < 16 ? 2 * RMAX + 1 : 2 * RMAX; }
+
 template <int KB, int VB, int D, int RMAX>
 struct alignas(16) Smem {
-    f16 q[RMAX][D + 8];                    // the slice's queries, one row per head
-    f16 aq[2 * RMAX][D + 8];               // q*s of the current key group, hi/lo rows
+    f16 q[RMAX + 1][D + 8];                // the slice's queries, one row per head
+    f16 aq[operand_rows<RMAX>()][D + 8];   // q*s of the current key group, hi/lo rows
     f16 kz[D];                             // zeros of the current key group
     uint32_t kc[KB][D];                    // key codes of a 32-token block
     uint32_t vc[VB * D / 32][kVcStride];   // value codes, [word column][row]
     f16 vz[4][kTokStride];                 // value zeros, [group][row]
     float vs[4][32 + 4];                   // value scales, [group][row]
-    f16 ap[4][2 * RMAX][kTokStride];       // p*s per value group, hi/lo rows
-    f16 apz[2 * RMAX][kTokStride];         // p, hi/lo rows
+    f16 ap[4][operand_rows<RMAX>()][kTokStride];   // p*s per value group, hi/lo rows
+    f16 apz[operand_rows<RMAX>()][kTokStride];     // p, hi/lo rows
 };
 
 // Per-wave running softmax state and output accumulators for the two heads
@@ -257,7 +262,7 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Acc<D>& ac
 #pragma clang diagnostic ignored "-Wpass-failed"
 template <int KB, int VB, int D, int G, int RMAX>
 __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8))) attention_kernel(const AttnArgs a) {
-    constexpr int NK32 = D / 32, NT16 = D / 16, ROWS = 2 * RMAX;
+    constexpr int NK32 = D / 32, NT16 = D / 16, ROWS = 2 * RMAX, OROWS = operand_rows<RMAX>();
     __shared__ Smem<KB, VB, D, RMAX> sm;
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
     const int r = a.q_per_kv;
@@ -269,28 +274,24 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     const int n_quant_s = a.n_quant_s ? min(max(a.n_quant_s[s], 0), a.n_quant) : a.n_quant;
     const int res_count_s = a.res_count_s ? min(max(a.res_count_s[s], 0), a.res_count) : a.res_count;
 
-    // operand rows that are never written stay zero
-    for (int i = L; i < ROWS * (D + 8); i += kWave) (&sm.aq[0][0])[i] = (f16)0;
-    for (int i = L; i < 4 * ROWS * kTokStride; i += kWave) (&sm.ap[0][0][0])[i] = (f16)0;
-    for (int i = L; i < ROWS * kTokStride; i += kWave) (&sm.apz[0][0])[i] = (f16)0;
-    // the queries to LDS; rows of heads >= r are zero
-    for (int i = L; i < RMAX * D / 8; i += kWave) {
+    // operand rows that are never written (and the zero rows) stay zero
+    for (int i = L; i < OROWS * (D + 8); i += kWave) (&sm.aq[0][0])[i] = (f16)0;
+    for (int i = L; i < 4 * OROWS * kTokStride; i += kWave) (&sm.ap[0][0][0])[i] = (f16)0;
+    for (int i = L; i < OROWS * kTokStride; i += kWave) (&sm.apz[0][0])[i] = (f16)0;
+    // the queries to LDS; rows of heads >= r and the zero row are zero
+    for (int i = L; i < (RMAX + 1) * D / 8; i += kWave) {
         const int h = i / (D / 8), c = 8 * (i - h * (D / 8));
         u32x4 w = u32x4{0, 0, 0, 0};
-        if (h < r) w = *reinterpret_cast<const u32x4*>(a.q + (s * r + h) * D + c);
+        if (h < r && h < RMAX) w = *reinterpret_cast<const u32x4*>(a.q + (s * r + h) * D + c);
         *reinterpret_cast<u32x4*>(&sm.q[h][c]) = w;
     }
-    // A-operand rows: lane row j; rows >= ROWS are zero without an LDS read
-    const bool row_live = j < ROWS;
-    const int jr = row_live ? j : 0;
-    const h8 zero8 = __builtin_bit_cast(h8, u32x4{0, 0, 0, 0});
+    // A-operand rows: lane row j; lanes of rows >= ROWS read the zero row
+    // (there are none when ROWS = 16)
+    const int jr = j < ROWS ? j : OROWS - 1;
     // q as MFMA A operand, rows 2h = q_h and 2h+1 = 0: lane row j, channels
     // 32*kk + 8*kq .. +7
-    const bool qrow_live = (j & 1) == 0 && (j >> 1) < RMAX;
-    auto qa = [&](int kk) {
-        const h8 v = lds_h8(&sm.q[qrow_live ? j >> 1 : 0][32 * kk + 8 * kq]);
-        return qrow_live ? v : zero8;
-    };
+    const int qr = ((j & 1) == 0 && (j >> 1) < RMAX) ? j >> 1 : RMAX;
+    auto qa = [&](int kk) { return lds_h8(&sm.q[qr][32 * kk + 8 * kq]); };
 
     Acc<D> acc;
     acc.m_a = acc.m_b = kNegInf;
@@ -330,7 +331,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             softmax_block(acc, xa, xb);
             weights_to_lds(sm, xa, xb, r);
             // values: B[token 8kq+e][channel 16nt+j]
-            const h8 pa8 = row_live ? lds_h8(&sm.apz[jr][8 * kq]) : zero8;
+            const h8 pa8 = lds_h8(&sm.apz[jr][8 * kq]);
             const uint16_t* vrow[8];
             bool valid[8];
 #pragma unroll
@@ -495,7 +496,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         f4 sc[2] = {f4{0, 0, 0, 0}, f4{0, 0, 0, 0}};
 #pragma unroll
         for (int kk = 0; kk < NK32; ++kk) {
-            const h8 aop = row_live ? lds_h8(&sm.aq[jr][32 * kk + 8 * kq]) : zero8;
+            const h8 aop = lds_h8(&sm.aq[jr][32 * kk + 8 * kq]);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int wi = (16 * tt + j) / (32 / KB);
@@ -541,14 +542,14 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         lds_order();
         // values: zero-point term over all groups at once (columns = groups)
         {
-            const h8 pz = row_live ? lds_h8(&sm.apz[jr][8 * kq]) : zero8;
+            const h8 pz = lds_h8(&sm.apz[jr][8 * kq]);
             const h8 bz = lds_h8(&sm.vz[j < ngv ? j : 0][8 * kq]);
             acc.z = mfma(pz, j < ngv ? bz : __builtin_bit_cast(h8, u32x4{0, 0, 0, 0}), acc.z);
         }
 #pragma unroll
         for (int nt = 0; nt < NT16; ++nt) {
             const int gv = (16 * nt) / G;
-            const h8 aop = row_live ? lds_h8(&sm.ap[gv][jr][8 * kq]) : zero8;
+            const h8 aop = lds_h8(&sm.ap[gv][jr][8 * kq]);
             const int col = (16 * nt + j) / (32 / VB);
             const uint32_t* wp = &sm.vc[col][8 * kq];
             const h8 bop = codes8<VB>(*reinterpret_cast<const u32x4*>(wp),
