@@ -49,7 +49,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kTokStride = 32 + 8;        // halves per row of a 32-token operand
-constexpr int kVcStride = 32 + 4;         // words per transposed value-code column
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ f4 mfma(const h8& a, const h8& b, const f4& c) {
@@ -80,32 +79,45 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v + dpp_f<0x140>(v);
 }
 
+// Codes are staged in LDS byte-transposed: four words w0..w3 (four channels
+// of one key word row, or one value word column of four consecutive tokens)
+// become four dwords, dword b holding byte b of each word in the order
+// (w0, w2, w1, w3).  A lane's eight codes for one MFMA operand (eight
+// consecutive channels, or tokens, at one code position) then sit in two
+// dwords instead of eight words, which cuts the operand's LDS reads
+// fourfold, and the order lets a single AND pick out two of the codes.
+__device__ __forceinline__ u32x4 bytes_t4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    const uint32_t p = __builtin_amdgcn_perm(w2, w0, 0x05010400u);   // w0.0 w2.0 w0.1 w2.1
+    const uint32_t q = __builtin_amdgcn_perm(w2, w0, 0x07030602u);   // w0.2 w2.2 w0.3 w2.3
+    const uint32_t r = __builtin_amdgcn_perm(w3, w1, 0x05010400u);   // w1.0 w3.0 w1.1 w3.1
+    const uint32_t u = __builtin_amdgcn_perm(w3, w1, 0x07030602u);   // w1.2 w3.2 w1.3 w3.3
+    return u32x4{__builtin_amdgcn_perm(r, p, 0x05040100u),           // w0.0 w2.0 w1.0 w3.0
+                 __builtin_amdgcn_perm(r, p, 0x07060302u),           // w0.1 w2.1 w1.1 w3.1
+                 __builtin_amdgcn_perm(u, q, 0x05040100u),           // w0.2 w2.2 w1.2 w3.2
+                 __builtin_amdgcn_perm(u, q, 0x07060302u)};          // w0.3 w2.3 w1.3 w3.3
+}
+
 // Where a lane's code sits: element m of a word (m = position along the
 // packing axis) occupies bits [BITS*m, BITS*m + BITS): byte bi, shift sh.
 template <int BITS>
 struct CodePos {
-    uint32_t sel;    // v_perm selector: byte bi of S1 -> byte 0, of S0 -> byte 2
+    int bi;          // byte of the word, i.e. dword of a transposed group of four
     uint32_t mask;   // the code in both 16-bit halves
     float col;       // 2^(24 - sh), undoes the subnormal encoding
     __device__ explicit CodePos(int m) {
         const int bit = BITS * m;
-        const int bi = bit >> 3, sh = bit & 7;
-        sel = (uint32_t)bi | (0x0Cu << 8) | ((uint32_t)(4 + bi) << 16) | (0x0Cu << 24);
+        const int sh = bit & 7;
+        bi = bit >> 3;
         mask = ((uint32_t)((1 << BITS) - 1) << sh) * 0x00010001u;
         col = pow2(24 - sh);
     }
 };
 
-// Eight codes (one per word, consecutive along the MFMA reduction axis) as
-// fp16 operands: element e from word e.
-template <int BITS>
-__device__ __forceinline__ h8 codes8(const u32x4& lo, const u32x4& hi, const CodePos<BITS>& cp) {
-    u32x4 r;
-    r.x = __builtin_amdgcn_perm(lo.y, lo.x, cp.sel) & cp.mask;
-    r.y = __builtin_amdgcn_perm(lo.w, lo.z, cp.sel) & cp.mask;
-    r.z = __builtin_amdgcn_perm(hi.y, hi.x, cp.sel) & cp.mask;
-    r.w = __builtin_amdgcn_perm(hi.w, hi.z, cp.sel) & cp.mask;
-    return __builtin_bit_cast(h8, r);
+// Eight codes as fp16 operands from two transposed dwords d0 (elements
+// 0..3) and d1 (4..7): code c at shift sh becomes the fp16 bit pattern
+// c << sh, the exact subnormal c * 2^(sh - 24).
+__device__ __forceinline__ h8 codes8(uint32_t d0, uint32_t d1, uint32_t mask) {
+    return __builtin_bit_cast(h8, u32x4{d0 & mask, (d0 >> 8) & mask, d1 & mask, (d1 >> 8) & mask});
 }
 
 // A wave's LDS instructions execute in program order, so one wave sharing
@@ -146,8 +158,8 @@ struct alignas(16) Smem {
     f16 q[RMAX + 1][D + 8];                // the slice's queries, one row per head
     f16 aq[operand_rows<RMAX>()][D + 8];   // q*s of the current key group, hi/lo rows
     f16 kz[D];                             // zeros of the current key group
-    uint32_t kc[KB][D];                    // key codes of a 32-token block
-    uint32_t vc[VB * D / 32][kVcStride];   // value codes, [word column][row]
+    uint32_t kt[KB][D];                    // key codes of a 32-token block: [word row][channel/4][byte]
+    uint32_t vt[VB * D / 32][32];          // value codes: [word column][token/4][byte]
     f16 vz[4][kTokStride];                 // value zeros, [group][row]
     float vs[4][32 + 4];                   // value scales, [group][row]
     f16 ap[4][operand_rows<RMAX>()][kTokStride];   // p*s per value group, hi/lo rows
@@ -372,7 +384,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     constexpr int WPT = NGV * G * VB / 32;                // value words per row
     const int ngk_cap = (a.cap_tokens + G - 1) / G;
     const int ngv = NGV, wpt = WPT;
-    constexpr int VPAIRS = D * VB / 64;                   // word pairs per row that hold real channels
+    constexpr int RW = D * VB / 32;                       // value words per row that hold real channels
     const uint32_t* kcs = a.k_codes + s * (int64_t)ngk_cap * Wk * D;
     const uint16_t* kss = a.k_scale + s * (int64_t)ngk_cap * D;
     const uint16_t* kzs = a.k_zero + s * (int64_t)ngk_cap * D;
@@ -385,10 +397,11 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     // compute until it is written to LDS (so its load latency is hidden).
     constexpr int KCH = KB * D / 4;                       // 16-byte key-code chunks per block
     constexpr int KV = (KCH + kWave - 1) / kWave;
-    constexpr int VV = (32 * VPAIRS + kWave - 1) / kWave; // value-code word pairs per lane
+    constexpr int VU = 8 * RW;                            // value units: one word column of 4 tokens
+    constexpr int VV = (VU + kWave - 1) / kWave;
     struct Stage {
         u32x4 k[KV];
-        uint32_t v[VV][2];
+        uint32_t v[VV][4];
         uint16_t vsb[(32 * NGV + kWave - 1) / kWave], vzb[(32 * NGV + kWave - 1) / kWave];
         uint32_t ks, kz;
     };
@@ -402,13 +415,15 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         }
 #pragma unroll
         for (int i = 0; i < VV; ++i) {
-            const int e = L + kWave * i;
-            if (32 * VPAIRS % kWave == 0 || e < 32 * VPAIRS) {
-                const int row = e / VPAIRS, c2 = 2 * (e - row * VPAIRS);
-                const int t = min(t0 + row, n - 1);       // rows past n: masked at commit
-                const uint32_t* src = vcs + (int64_t)t * WPT + c2;
-                st.v[i][0] = __builtin_nontemporal_load(src);
-                st.v[i][1] = __builtin_nontemporal_load(src + 1);
+            const int u = L + kWave * i;
+            if (VU % kWave == 0 || u < VU) {
+                const int c2 = u >> 3, q = u & 7;         // word column, token quad
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // rows past n: any valid row; their weights are 0
+                    const int t = min(t0 + 4 * q + e, n - 1);
+                    st.v[i][e] = __builtin_nontemporal_load(vcs + (int64_t)t * WPT + c2);
+                }
             }
         }
 #pragma unroll
@@ -433,17 +448,16 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             const int v = L + kWave * i;
             if (KCH % kWave == 0 || v < KCH) {
                 const int row = (4 * v) / D, col = (4 * v) % D;
-                *reinterpret_cast<u32x4*>(&sm.kc[row][col]) = st.k[i];
+                const u32x4& w = st.k[i];
+                *reinterpret_cast<u32x4*>(&sm.kt[row][col]) = bytes_t4(w.x, w.y, w.z, w.w);
             }
         }
 #pragma unroll
         for (int i = 0; i < VV; ++i) {
-            const int e = L + kWave * i;
-            if (32 * VPAIRS % kWave == 0 || e < 32 * VPAIRS) {
-                const int row = e / VPAIRS, c2 = 2 * (e - row * VPAIRS);
-                const bool live = t0 + row < n;
-                sm.vc[c2][row] = live ? st.v[i][0] : 0u;
-                sm.vc[c2 + 1][row] = live ? st.v[i][1] : 0u;
+            const int u = L + kWave * i;
+            if (VU % kWave == 0 || u < VU) {
+                const uint32_t* w = st.v[i];
+                *reinterpret_cast<u32x4*>(&sm.vt[0][0] + 4 * u) = bytes_t4(w[0], w[1], w[2], w[3]);
             }
         }
 #pragma unroll
@@ -500,9 +514,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int wi = (16 * tt + j) / (32 / KB);
-                const uint32_t* wp = &sm.kc[wi][32 * kk + 8 * kq];
-                const h8 bop = codes8<KB>(*reinterpret_cast<const u32x4*>(wp),
-                                          *reinterpret_cast<const u32x4*>(wp + 4), kpos);
+                const uint32_t* dp = &sm.kt[wi][32 * kk + 8 * kq + kpos.bi];
+                const h8 bop = codes8(dp[0], dp[4], kpos.mask);
                 sc[tt] = mfma(aop, bop, sc[tt]);
             }
         }
@@ -551,9 +564,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             const int gv = (16 * nt) / G;
             const h8 aop = lds_h8(&sm.ap[gv][jr][8 * kq]);
             const int col = (16 * nt + j) / (32 / VB);
-            const uint32_t* wp = &sm.vc[col][8 * kq];
-            const h8 bop = codes8<VB>(*reinterpret_cast<const u32x4*>(wp),
-                                      *reinterpret_cast<const u32x4*>(wp + 4), vpos);
+            const uint32_t* dp = &sm.vt[col][8 * kq + vpos.bi];
+            const h8 bop = codes8(dp[0], dp[4], vpos.mask);
             acc.o[nt] = mfma(aop, bop, acc.o[nt]);
         }
         lds_order();   // the next block's commit overwrites what this one read
