@@ -79,6 +79,20 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v + dpp_f<0x140>(v);
 }
 
+// Sum over the whole wave (every lane gets the total): row sums, then the
+// four rows' totals read out as uniform values.
+__device__ __forceinline__ float wave_sum(float v) {
+    const int b = __builtin_bit_cast(int, row16_sum(v));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float lo_f(uint32_t w) { return (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xFFFF)); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return (float)__builtin_bit_cast(f16, (uint16_t)(w >> 16)); }
+
 // Codes are staged in LDS byte-transposed: four words w0..w3 (four channels
 // of one key word row, or one value word column of four consecutive tokens)
 // become four dwords, dword b holding byte b of each word in the order
@@ -392,6 +406,21 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     const uint16_t* vss = a.v_scale + s * (int64_t)a.cap_tokens * ngv;
     const uint16_t* vzs = a.v_zero + s * (int64_t)a.cap_tokens * ngv;
     const bool pair_live = 2 * L < D;                     // this lane's channel pair (2L, 2L+1) exists
+    // At most two heads: this lane's query channels (2L, 2L+1) of heads 0
+    // and 1 stay in registers (0 where absent), and a key group's zero-point
+    // term sum_d q_d z_d is a dot product over the wave (fp32, as the MFMA
+    // would accumulate it) instead of four MFMAs and their LDS operands.
+    float qreg[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+    float zg0 = 0.0f, zg1 = 0.0f;                         // zero terms of heads 0 and 1
+    if constexpr (RMAX == 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            if (h < r && pair_live) {
+                const uint32_t qw = *reinterpret_cast<const uint32_t*>(a.q + (s * r + h) * D + 2 * L);
+                qreg[h][0] = lo_f(qw);
+                qreg[h][1] = hi_f(qw);
+            }
+    }
 
     // One block's global data, held in registers from the previous block's
     // compute until it is written to LDS (so its load latency is hidden).
@@ -471,9 +500,27 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             }
         }
         // a new key group: q*s operand rows (fp32 product split hi/lo) and zeros
-        if ((t0 % G == 0 || blk == b0) && pair_live) {
-            const float s0 = (float)__builtin_bit_cast(f16, (uint16_t)(st.ks & 0xFFFF));
-            const float s1 = (float)__builtin_bit_cast(f16, (uint16_t)(st.ks >> 16));
+        if constexpr (RMAX == 2) {
+            if (t0 % G == 0 || blk == b0) {
+                const float z0 = pair_live ? lo_f(st.kz) : 0.0f, z1 = pair_live ? hi_f(st.kz) : 0.0f;
+                zg0 = wave_sum(__builtin_fmaf(qreg[0][1], z1, qreg[0][0] * z0));
+                zg1 = r > 1 ? wave_sum(__builtin_fmaf(qreg[1][1], z1, qreg[1][0] * z0)) : 0.0f;
+                if (pair_live) {
+                    const float s0 = lo_f(st.ks), s1 = hi_f(st.ks);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        if (h < r) {
+                            f16 h0, l0, h1, l1;
+                            split_hl(qreg[h][0] * s0, h0, l0);
+                            split_hl(qreg[h][1] * s1, h1, l1);
+                            *reinterpret_cast<uint32_t*>(&sm.aq[2 * h][2 * L]) = pack_h2(h0, h1);
+                            *reinterpret_cast<uint32_t*>(&sm.aq[2 * h + 1][2 * L]) = pack_h2(l0, l1);
+                        }
+                    }
+                }
+            }
+        } else if ((t0 % G == 0 || blk == b0) && pair_live) {
+            const float s0 = lo_f(st.ks), s1 = hi_f(st.ks);
             *reinterpret_cast<uint32_t*>(&sm.kz[2 * L]) = st.kz;
             for (int h = 0; h < r; ++h) {
                 const uint32_t qw = *reinterpret_cast<const uint32_t*>(&sm.q[h][2 * L]);
@@ -502,7 +549,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
 
         // keys: the zero-point term of a new group, then the scores of two
         // 16-token tiles
-        if (t0 % G == 0 || blk == b0) {
+        if (RMAX != 2 && (t0 % G == 0 || blk == b0)) {
             zk = f4{0, 0, 0, 0};
 #pragma unroll
             for (int kk = 0; kk < NK32; ++kk) zk = mfma(qa(kk), lds_h8(&sm.kz[32 * kk + 8 * kq]), zk);
@@ -520,11 +567,12 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             }
         }
         float xa[2], xb[2];
+        const float za = RMAX == 2 ? zg0 : zk[0], zb = RMAX == 2 ? zg1 : zk[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const bool valid = t0 + 16 * tt + j < n;
-            xa[tt] = valid ? ((sc[tt][0] + sc[tt][1]) * kpos.col + zk[0]) * a.logit_scale : kNegInf;
-            xb[tt] = valid ? ((sc[tt][2] + sc[tt][3]) * kpos.col + zk[2]) * a.logit_scale : kNegInf;
+            xa[tt] = valid ? ((sc[tt][0] + sc[tt][1]) * kpos.col + za) * a.logit_scale : kNegInf;
+            xb[tt] = valid ? ((sc[tt][2] + sc[tt][3]) * kpos.col + zb) * a.logit_scale : kNegInf;
         }
         softmax_block(acc, xa, xb);
 
