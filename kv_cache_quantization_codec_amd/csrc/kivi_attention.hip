@@ -90,6 +90,13 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// base + a 32-bit byte offset: with a wave-uniform base the load can take
+// the scalar-base form, and the lane's address arithmetic stays 32-bit.
+template <class T>
+__device__ __forceinline__ const T* at_byte(const T* base, uint32_t off) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off);
+}
+
 __device__ __forceinline__ float lo_f(uint32_t w) { return (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xFFFF)); }
 __device__ __forceinline__ float hi_f(uint32_t w) { return (float)__builtin_bit_cast(f16, (uint16_t)(w >> 16)); }
 
@@ -173,8 +180,8 @@ struct alignas(16) Smem {
     f16 aq[operand_rows<RMAX>()][D + 8];   // q*s of the current key group, hi/lo rows
     f16 kz[D];                             // zeros of the current key group
     uint32_t kt[KB][D];                    // key codes of a 32-token block: [word row][channel/4][byte]
-    uint32_t vt[VB * D / 32][32];          // value codes: [word column][token/4][byte]
-    f16 vz[4][kTokStride];                 // value zeros, [group][row]
+    uint32_t vt[VB * D / 32][32];          // value codes: [word column][token unit][byte]
+    f16 vz[4][kTokStride];                 // value zeros, [group][operand slot of the row]
     float vs[4][32 + 4];                   // value scales, [group][row]
     f16 ap[4][operand_rows<RMAX>()][kTokStride];   // p*s per value group, hi/lo rows
     f16 apz[operand_rows<RMAX>()][kTokStride];     // p, hi/lo rows
@@ -434,24 +441,32 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         uint16_t vsb[(32 * NGV + kWave - 1) / kWave], vzb[(32 * NGV + kWave - 1) / kWave];
         uint32_t ks, kz;
     };
+    // Addresses: wave-uniform bases of the block (64-bit, scalar) plus lane
+    // byte offsets below 2^32 (at most 32 rows of one block).
     auto load = [&](int blk, Stage& st) {
         const int t0 = 32 * blk, g = t0 / G;
+        const int last = n - 1 - t0;                      // rows past n read row n-1 (weights 0)
         const uint32_t* srck = kcs + ((int64_t)g * Wk + ((t0 % G) / 32) * KB) * D;
+        const uint32_t* vrow = vcs + (int64_t)t0 * WPT;
+        const uint16_t* srow = vss + (int64_t)t0 * NGV;
+        const uint16_t* zrow = vzs + (int64_t)t0 * NGV;
 #pragma unroll
         for (int i = 0; i < KV; ++i) {
             const int v = L + kWave * i;
-            if (KCH % kWave == 0 || v < KCH) st.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(srck) + v);
+            if (KCH % kWave == 0 || v < KCH)
+                st.k[i] = __builtin_nontemporal_load(at_byte(reinterpret_cast<const u32x4*>(srck), 16u * v));
         }
 #pragma unroll
         for (int i = 0; i < VV; ++i) {
             const int u = L + kWave * i;
             if (VU % kWave == 0 || u < VU) {
-                const int c2 = u >> 3, q = u & 7;         // word column, token quad
+                // word column c2, tokens 2p, 16 + 2p, 2p + 1, 17 + 2p (the
+                // value product's token order, see below)
+                const int c2 = u >> 3, p = u & 7;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    // rows past n: any valid row; their weights are 0
-                    const int t = min(t0 + 4 * q + e, n - 1);
-                    st.v[i][e] = __builtin_nontemporal_load(vcs + (int64_t)t * WPT + c2);
+                    const int row = min(2 * p + (e >> 1) + 16 * (e & 1), last);
+                    st.v[i][e] = __builtin_nontemporal_load(at_byte(vrow, 4u * (uint32_t)(row * WPT + c2)));
                 }
             }
         }
@@ -460,14 +475,14 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             const int e = L + kWave * i;
             if (32 * NGV % kWave == 0 || e < 32 * NGV) {
                 const int row = e / NGV, gv = e - row * NGV;
-                const int t = min(t0 + row, n - 1);       // rows past n: any valid row, masked below
-                st.vsb[i] = vss[(int64_t)t * NGV + gv];
-                st.vzb[i] = vzs[(int64_t)t * NGV + gv];
+                const uint32_t off = 2u * (uint32_t)(min(row, last) * NGV + gv);   // masked below
+                st.vsb[i] = *at_byte(srow, off);
+                st.vzb[i] = *at_byte(zrow, off);
             }
         }
         if ((t0 % G == 0 || blk == b0) && pair_live) {
-            st.ks = *reinterpret_cast<const uint32_t*>(kss + (int64_t)g * D + 2 * L);
-            st.kz = *reinterpret_cast<const uint32_t*>(kzs + (int64_t)g * D + 2 * L);
+            st.ks = *at_byte(reinterpret_cast<const uint32_t*>(kss + (int64_t)g * D), 4u * L);
+            st.kz = *at_byte(reinterpret_cast<const uint32_t*>(kzs + (int64_t)g * D), 4u * L);
         }
     };
     auto commit = [&](int blk, const Stage& st) {
@@ -496,7 +511,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
                 const int row = e / NGV, gv = e - row * NGV;
                 const bool live = t0 + row < n;
                 sm.vs[gv][row] = live ? (float)__builtin_bit_cast(f16, st.vsb[i]) : 0.0f;
-                sm.vz[gv][row] = __builtin_bit_cast(f16, live ? st.vzb[i] : (uint16_t)0);
+                sm.vz[gv][2 * (row & 15) + (row >> 4)] = __builtin_bit_cast(f16, live ? st.vzb[i] : (uint16_t)0);
             }
         }
         // a new key group: q*s operand rows (fp32 product split hi/lo) and zeros
@@ -576,27 +591,27 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         }
         softmax_block(acc, xa, xb);
 
-        // values: each lane turns its own weights (tokens 16tt + j, heads
-        // 2kq and 2kq+1) into the hi/lo operand rows of p and of p*s for
-        // every value group, straight from registers
+        // values: the product runs over the block's tokens in the order
+        // 0, 16, 1, 17, ..., 15, 31 (operand slot 2m is token m, slot 2m + 1
+        // token 16 + m), so the two weights a lane holds (tokens j and
+        // 16 + j of heads 2kq and 2kq+1) fill one dword of each hi/lo
+        // operand row: p itself, and p*s for every value group
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int h = 2 * kq + hh;
             if (h < r) {
+                const float p0 = hh ? xb[0] : xa[0], p1 = hh ? xb[1] : xa[1];
+                f16 h0, l0, h1, l1;
+                split_hl(p0, h0, l0);
+                split_hl(p1, h1, l1);
+                *reinterpret_cast<uint32_t*>(&sm.apz[2 * h][2 * j]) = pack_h2(h0, h1);
+                *reinterpret_cast<uint32_t*>(&sm.apz[2 * h + 1][2 * j]) = pack_h2(l0, l1);
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt) {
-                    const int t = 16 * tt + j;
-                    const float p = hh ? xb[tt] : xa[tt];
-                    f16 hi, lo;
-                    split_hl(p, hi, lo);
-                    sm.apz[2 * h][t] = hi;
-                    sm.apz[2 * h + 1][t] = lo;
-#pragma unroll
-                    for (int gv = 0; gv < NGV; ++gv) {
-                        split_hl(p * sm.vs[gv][t], hi, lo);
-                        sm.ap[gv][2 * h][t] = hi;
-                        sm.ap[gv][2 * h + 1][t] = lo;
-                    }
+                for (int gv = 0; gv < NGV; ++gv) {
+                    split_hl(p0 * sm.vs[gv][j], h0, l0);
+                    split_hl(p1 * sm.vs[gv][16 + j], h1, l1);
+                    *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h][2 * j]) = pack_h2(h0, h1);
+                    *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h + 1][2 * j]) = pack_h2(l0, l1);
                 }
             }
         }
