@@ -45,6 +45,7 @@ namespace {
 typedef _Float16 f16;
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -161,6 +162,20 @@ __device__ __forceinline__ h8 lds_h8(const void* p) {
 __device__ __forceinline__ void split_hl(float x, f16& hi, f16& lo) {
     hi = (f16)x;
     lo = (f16)(x - (float)hi);
+}
+
+// Two products x_i = a_i * b_i (exact, fused) split as packed pairs
+// hi = (fp16(x0), fp16(x1)) and lo = (fp16(x0 - hi0), fp16(x1 - hi1)): the
+// mixed-precision FMAs write one 16-bit half each and read hi's halves
+// directly, four instructions in all.  hi + lo is within 2^-22 |x_i| of x_i.
+__device__ __forceinline__ void split_prod2(float a0, float b0, float a1, float b1, uint32_t& hi,
+                                            uint32_t& lo) {
+    __asm__("v_fma_mixlo_f16 %0, %2, %3, 0\n\t"
+            "v_fma_mixhi_f16 %0, %4, %5, 0\n\t"
+            "v_fma_mixlo_f16 %1, %2, %3, -%0 op_sel_hi:[0,0,1]\n\t"
+            "v_fma_mixhi_f16 %1, %4, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+            : "=&v"(hi), "=&v"(lo)
+            : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
 
 // LDS of one wave (D = head_dim, at most RMAX query heads per KV slice, so
@@ -525,11 +540,10 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         if (h < r) {
-                            f16 h0, l0, h1, l1;
-                            split_hl(qreg[h][0] * s0, h0, l0);
-                            split_hl(qreg[h][1] * s1, h1, l1);
-                            *reinterpret_cast<uint32_t*>(&sm.aq[2 * h][2 * L]) = pack_h2(h0, h1);
-                            *reinterpret_cast<uint32_t*>(&sm.aq[2 * h + 1][2 * L]) = pack_h2(l0, l1);
+                            uint32_t hi, lo;
+                            split_prod2(qreg[h][0], s0, qreg[h][1], s1, hi, lo);
+                            *reinterpret_cast<uint32_t*>(&sm.aq[2 * h][2 * L]) = hi;
+                            *reinterpret_cast<uint32_t*>(&sm.aq[2 * h + 1][2 * L]) = lo;
                         }
                     }
                 }
@@ -539,13 +553,10 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             *reinterpret_cast<uint32_t*>(&sm.kz[2 * L]) = st.kz;
             for (int h = 0; h < r; ++h) {
                 const uint32_t qw = *reinterpret_cast<const uint32_t*>(&sm.q[h][2 * L]);
-                const float q0 = (float)__builtin_bit_cast(f16, (uint16_t)(qw & 0xFFFF));
-                const float q1 = (float)__builtin_bit_cast(f16, (uint16_t)(qw >> 16));
-                f16 h0, l0, h1, l1;
-                split_hl(q0 * s0, h0, l0);
-                split_hl(q1 * s1, h1, l1);
-                *reinterpret_cast<uint32_t*>(&sm.aq[2 * h][2 * L]) = pack_h2(h0, h1);
-                *reinterpret_cast<uint32_t*>(&sm.aq[2 * h + 1][2 * L]) = pack_h2(l0, l1);
+                uint32_t hi, lo;
+                split_prod2(lo_f(qw), s0, hi_f(qw), s1, hi, lo);
+                *reinterpret_cast<uint32_t*>(&sm.aq[2 * h][2 * L]) = hi;
+                *reinterpret_cast<uint32_t*>(&sm.aq[2 * h + 1][2 * L]) = lo;
             }
         }
     };
@@ -601,17 +612,15 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             const int h = 2 * kq + hh;
             if (h < r) {
                 const float p0 = hh ? xb[0] : xa[0], p1 = hh ? xb[1] : xa[1];
-                f16 h0, l0, h1, l1;
-                split_hl(p0, h0, l0);
-                split_hl(p1, h1, l1);
-                *reinterpret_cast<uint32_t*>(&sm.apz[2 * h][2 * j]) = pack_h2(h0, h1);
-                *reinterpret_cast<uint32_t*>(&sm.apz[2 * h + 1][2 * j]) = pack_h2(l0, l1);
+                uint32_t hi, lo;
+                split_prod2(p0, 1.0f, p1, 1.0f, hi, lo);
+                *reinterpret_cast<uint32_t*>(&sm.apz[2 * h][2 * j]) = hi;
+                *reinterpret_cast<uint32_t*>(&sm.apz[2 * h + 1][2 * j]) = lo;
 #pragma unroll
                 for (int gv = 0; gv < NGV; ++gv) {
-                    split_hl(p0 * sm.vs[gv][j], h0, l0);
-                    split_hl(p1 * sm.vs[gv][16 + j], h1, l1);
-                    *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h][2 * j]) = pack_h2(h0, h1);
-                    *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h + 1][2 * j]) = pack_h2(l0, l1);
+                    split_prod2(p0, sm.vs[gv][j], p1, sm.vs[gv][16 + j], hi, lo);
+                    *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h][2 * j]) = hi;
+                    *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h + 1][2 * j]) = lo;
                 }
             }
         }
