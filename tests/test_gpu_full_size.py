@@ -130,3 +130,118 @@ def test_stream_batch64_full_size_sampled():
     for i in range(w.steps):
         sr.append(knh[i], vnh[i])
     compare_stream(st, sr, slices=picks)
+
+
+# ---- next rows at their full sizes ------------------------------------------
+
+@pytest.mark.parametrize("name", ["llama2_7b_2bit", "mistral_7b_k2v4"])
+def test_attention_full_size_sampled(name):
+    """Decode attention over the whole cache in one call (the split plan the
+    benchmark times).  Sampled slices: the oracle's attention over the
+    oracle's own encoding of those slices, within the derived tolerance.
+    Every slice: outputs are finite and lie within the range of the slice's
+    values widened by half a quantization step (a weighted mean of
+    dequantized values cannot leave it)."""
+    from kvsynth import decode_queries
+    from oracle import attention_ref as att
+    from tests.test_gpu_attention import _bound
+
+    w = WORKLOADS[name]
+    cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
+    n, R, S, D, G = w.tokens - w.residual_length, w.residual_length, w.slices, w.head_dim, w.group_size
+    _log(f"{name} attention: generating S={S} T={w.tokens}")
+    k, v = full_cache(w)
+    kq, vq = K.alloc_keys(cfg, S, n), K.alloc_values(cfg, S, n)
+    K.kivi_encode_k(cfg, k, n, *kq)
+    K.kivi_encode_v(cfg, v, n, *vq)
+    q = decode_queries(w, "cuda")
+    out = torch.full_like(q, float("nan"))
+    sm_scale = D ** -0.5
+    cache = K.AttnCache(cfg, kq, vq, n, k[:, n:], v[:, n:], 0, R)
+    ws = K.kivi_attention_workspace_bytes(cfg, S, w.q_per_kv, n, R)
+    n_splits = max(1, ws // (S * w.q_per_kv * (D + 2) * 4))
+    _log(f"{name} attention: one call, {n_splits} splits per slice")
+    K.kivi_decode_attention(cfg, cache, q, sm_scale, out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    # every slice: within [min v - step/2, max v + step/2] per channel
+    b = w.v_bits
+    for s0 in range(0, S, 512):
+        vs = v[s0:s0 + 512].float()
+        lo, hi = vs.min(dim=1).values, vs.max(dim=1).values                    # [s, D]
+        step = (vs.amax(dim=(1, 2)) - vs.amin(dim=(1, 2))) / (2 ** b - 1)      # [s]
+        pad = (0.5 * step * 1.01)[:, None, None] + 2.0 ** -10 * torch.maximum(lo.abs(), hi.abs())[:, None, :]
+        o = out[s0:s0 + 512].float()
+        assert bool((o >= lo[:, None, :] - pad).all() and (o <= hi[:, None, :] + pad).all()), \
+            f"slices {s0}..{s0 + 512}: output outside the value range"
+    picks = sample_slices(S, w.number + 100)
+    _log(f"{name} attention: oracle on slices {picks}")
+    kh, vh = U.bits16(k[picks]).view(F16), U.bits16(v[picks]).view(F16)
+    kp = ref.encode_k(kh, n, w.k_bits, G)
+    vp = ref.encode_v(vh, n, w.v_bits, G)
+    qh = U.bits16(q[picks]).view(F16)
+    want = att.decode_attention(qh, kp, vp, n, kh[:, n:], vh[:, n:], w.k_bits, w.v_bits, G, sm_scale)
+    tol = _bound(qh, kp, vp, n, kh[:, n:], vh[:, n:], w.k_bits, w.v_bits, G, sm_scale, want, n_splits)
+    got = out[picks].float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - want)
+    assert np.all(err <= tol), f"max err/tol {np.max(err / tol):.3g}"
+    _log(f"{name} attention: max err/tol {np.max(err / tol):.3g}")
+
+
+def test_k8v4_full_size_sampled():
+    """FP8 keys and one-group 4-bit values of the whole Llama-shaped cache in
+    the benchmark's launches; sampled slices bit-exact against the oracle."""
+    from oracle import fp8_ref as f8
+
+    w = WORKLOADS["llama2_7b_k8v4"]
+    cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
+    n, S, D = w.tokens - w.residual_length, w.slices, w.head_dim
+    _log(f"k8v4: generating S={S} T={w.tokens}")
+    k, v = full_cache(w)
+    kq = torch.full((S, n, D), 0x5A, dtype=torch.uint8, device="cuda")
+    K.kivi_fp8_encode(k, n, kq)
+    kd = U.poisoned(torch.empty((S, n + 2, D), dtype=torch.float16, device="cuda"))
+    K.kivi_fp8_decode(kq, n, kd)
+    vq = U.gpu_encode("v", cfg, v, n)
+    torch.cuda.synchronize()
+    picks = sample_slices(S, 55)
+    _log(f"k8v4: oracle on slices {picks}")
+    kh = U.bits16(k[picks]).view(F16)
+    want = f8.encode_keys(kh, n)
+    assert np.array_equal(kq[picks].cpu().numpy(), want)
+    assert np.array_equal(U.bits16(kd[picks][:, :n]), f8.decode(want).view(np.uint16))
+    assert U.is_poison(U.bits16(kd[picks][:, n:]))
+    vh = U.bits16(v[picks]).view(F16)
+    pc, ps, pz = ref.encode_v(vh, n, w.v_bits, w.group_size)
+    U.assert_equal("value codes", U.words(vq[0][picks]), pc.view(np.uint32))
+    U.assert_equal("value scale", U.bits16(vq[1][picks]), ps.view(np.uint16))
+    U.assert_equal("value zero", U.bits16(vq[2][picks]), pz.view(np.uint16))
+
+
+def test_layer_mix_full_size_sampled():
+    """The 32-layer mix (first and last two layers at 8/8 bits) coded by the
+    layer-wise calls in the benchmark's layout; sampled slices of every
+    layer bit-exact against the oracle at that layer's bits."""
+    from oracle import layer_mix_ref as mix
+
+    w = WORKLOADS["llama2_7b_mix"]
+    n, spl, T, D, G = w.tokens - w.residual_length, w.slices_per_layer, w.tokens, w.head_dim, w.group_size
+    bits = mix.layer_bits(w.layers, w.boundary, (w.k_bits, w.v_bits), w.boundary_bits)
+    cfgs = [K.Config(kb, vb, G, w.residual_length, D) for kb, vb in bits]
+    _log(f"mix: generating {w.layers} layers x {spl} slices, T={T}")
+    k, v = full_cache(w)
+    for keys, x in ((True, k), (False, v)):
+        lay = K.alloc_layers(cfgs, spl, n, "cuda", keys=keys)
+        (K.kivi_encode_k_layers if keys else K.kivi_encode_v_layers)(cfgs, x.view(w.layers, spl, T, D), n, lay)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(7 if keys else 8)
+        for l in range(w.layers):
+            picks = sorted({0, spl - 1, int(rng.integers(0, spl))})
+            xh = U.bits16(x[l * spl:(l + 1) * spl][picks]).view(F16)
+            b = bits[l][0 if keys else 1]
+            oc, os_, oz = (ref.encode_k if keys else ref.encode_v)(xh, n, b, G)
+            side = "key" if keys else "value"
+            U.assert_equal(f"layer {l} {side} codes", U.words(lay[l][0][picks]), oc.view(np.uint32))
+            U.assert_equal(f"layer {l} {side} scale", U.bits16(lay[l][1][picks]), os_.view(np.uint16))
+            U.assert_equal(f"layer {l} {side} zero", U.bits16(lay[l][2][picks]), oz.view(np.uint16))
+        del lay
