@@ -20,12 +20,15 @@
 //   about 22 bits; the two rows are added after the MFMA.
 // * A code c enters as the fp16 bit pattern c << sh, i.e. the subnormal (or
 //   lowest-binade) value c * 2^(sh-24), exact because c << sh < 2^11; sh is
-//   the code's bit offset inside its byte.  Extracting it costs one v_perm
-//   (pick the byte of two words) and one AND per pair of codes; the column
-//   factor 2^(24-sh) is applied to the fp32 result.
-// * The zero-point terms are separate MFMAs: q against the group's zeros
-//   (identical in every token column), and p against the rows' zeros, whose
-//   16 output columns hold up to 16 value groups at once.
+//   the code's bit offset inside its byte.  Codes are staged in LDS
+//   byte-transposed (see bytes_t4), so a lane's eight codes for one operand
+//   sit in two dwords and come out with one AND, or a shift and an AND, per
+//   pair; the column factor 2^(24-sh) is applied to the fp32 result.
+// * The value zero-point term is a separate MFMA: p against the rows'
+//   zeros, whose 16 output columns hold up to 16 value groups at once.  The
+//   key zero-point term (identical in every token column of a group) is an
+//   MFMA of q against the group's zeros when a KV slice serves 3-8 query
+//   heads, and an fp32 dot product reduced over the wave for 1-2.
 // * Online softmax in base 2 per 32-token block; heads live in MFMA rows, so
 //   each lane holds two heads' scores of one token and the row reductions
 //   are DPP moves inside a 16-lane row.
@@ -45,7 +48,6 @@ namespace {
 typedef _Float16 f16;
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -148,10 +150,6 @@ __device__ __forceinline__ h8 codes8(uint32_t d0, uint32_t d1, uint32_t mask) {
 // only stops the compiler from moving LDS accesses across the point.
 __device__ __forceinline__ void lds_order() { __asm__ __volatile__("" ::: "memory"); }
 
-__device__ __forceinline__ uint32_t pack_h2(f16 a, f16 b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
 // 16-byte LDS read as an MFMA operand.
 __device__ __forceinline__ h8 lds_h8(const void* p) {
     return __builtin_bit_cast(h8, *reinterpret_cast<const u32x4*>(p));
@@ -244,8 +242,9 @@ __device__ __forceinline__ void softmax_block(Acc<D>& acc, float xa[2], float xb
     acc.z[3] *= al_b;
 }
 
-// The block's softmax weights (this lane: tokens 16tt + j of heads 2kq and
-// 2kq+1) as hi/lo fp16 rows of the value operand apz ([2h / 2h+1][token]).
+// The residual block's softmax weights (this lane: tokens 16tt + j of heads
+// 2kq and 2kq+1) as hi/lo fp16 rows of the value operand apz ([2h / 2h+1]
+// [token]); the residual's value product runs in token order.
 template <class SM>
 __device__ __forceinline__ void weights_to_lds(SM& sm, const float pa[2], const float pb[2], int r) {
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
