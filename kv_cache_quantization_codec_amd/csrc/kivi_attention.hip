@@ -29,6 +29,8 @@
 //   key zero-point term (identical in every token column of a group) is an
 //   MFMA of q against the group's zeros when a KV slice serves 3-8 query
 //   heads, and an fp32 dot product reduced over the wave for 1-2.
+// * Three kernel variants by the bound on query heads per KV slice (2, 4,
+//   8) size the LDS operand rows.
 // * Online softmax in base 2 per 32-token block; heads live in MFMA rows, so
 //   each lane holds two heads' scores of one token and the row reductions
 //   are DPP moves inside a 16-lane row.
@@ -180,10 +182,11 @@ __device__ __forceinline__ void split_prod2(float a0, float b0, float a1, float 
 // 2*RMAX live MFMA rows).  When that leaves MFMA rows dead (2*RMAX < 16),
 // each A-operand array has one more row that is always zero: lanes of the
 // dead rows read it (one address, a broadcast), so operand reads need no
-// exec masking.  Row strides are padded
-// by 16 bytes so that the rows an MFMA operand read touches fall in
-// different banks.  Sizing the rows by RMAX keeps the multi-head case small
-// enough for LDS not to limit the number of resident waves.
+// exec masking.  Row strides are padded by 16 bytes so that the rows an
+// MFMA operand read touches fall in different banks.  The head bound RMAX
+// is 2, 4 or 8 (the smallest that covers q_per_kv): sizing the rows by it
+// keeps LDS from limiting the resident waves (multi-head 7.4 KB, 4 heads
+// 11.6 KB, 8 heads 17.4 KB per wave at head_dim 128).
 template <int RMAX>
 constexpr int operand_rows() { return 2 * RMAX < 16 ? 2 * RMAX + 1 : 2 * RMAX; }
 
@@ -690,6 +693,8 @@ int run_attention(const AttnArgs& a, hipStream_t st) {
     const int64_t groups = a.n_slices * a.plan.n_splits;
     if (a.q_per_kv <= 2)
         hipLaunchKernelGGL((attention_kernel<KB, VB, D, G, 2>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
+    else if (a.q_per_kv <= 4)
+        hipLaunchKernelGGL((attention_kernel<KB, VB, D, G, 4>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
     else
         hipLaunchKernelGGL((attention_kernel<KB, VB, D, G, 8>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
     hipError_t e = hipGetLastError();

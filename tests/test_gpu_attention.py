@@ -230,9 +230,10 @@ def test_zero_query_is_the_mean_of_all_values():
 
 def test_grouped_heads_match_smaller_groups_bitwise():
     """A head's result does not depend on which other heads share the call,
-    within one kernel variant: 1-2 heads per KV slice form one variant (the
-    key zero-point term is a wave reduction), 3-8 another (it is an MFMA
-    product); the two differ only in that sum's order."""
+    within one zero-point formulation: with 1-2 heads per KV slice the key
+    zero-point term is a wave reduction, with 3-8 an MFMA product (kernel
+    variants for at most 4 and at most 8 heads share that arithmetic); the
+    two formulations differ only in that sum's order."""
     S, n, n_res, D = 3, 700, 40, 128
     k, v, q = _gen(99, S, n, n_res, D, 4)
     got2, _ = run_case(2, 4, 32, D, 2, n, n_res, q=q[:, :2], k=k, v=v)
@@ -243,6 +244,9 @@ def test_grouped_heads_match_smaller_groups_bitwise():
     for lo in (0, 1):
         got3, _ = run_case(2, 4, 32, D, 3, n, n_res, q=q[:, lo:lo + 3], k=k, v=v)
         assert np.array_equal(got4[:, lo:lo + 3], got3)
+    q8 = np.concatenate([q, q[:, ::-1]], axis=1)                   # 8 heads: the 8-head variant
+    got8, _ = run_case(2, 4, 32, D, 8, n, n_res, q=q8, k=k, v=v)
+    assert np.array_equal(got8[:, :4], got4)
 
 
 def test_stream_cache_after_prefill_and_steps():
