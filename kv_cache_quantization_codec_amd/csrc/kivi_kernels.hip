@@ -254,6 +254,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 
 constexpr int kNontemporal = 2;   // buffer-load cache policy: streaming, do not keep
 
+// XCD-aware block order.  MI355X has 8 XCDs (each with its own L2), and the
+// dispatcher hands workgroup i to XCD i mod 8, so with the identity order
+// neighbouring work items (neighbouring stretches of HBM) go to eight
+// different XCDs.  This returns the work item of this workgroup such that
+// each XCD takes runs of RUN consecutive items: within every super-chunk of
+// 8*RUN workgroups, XCD x gets items [x*RUN, x*RUN + RUN).  Workgroups past
+// the last whole super-chunk keep their own index, so the map is a bijection
+// of [0, gridDim.x) and a grid-stride loop over it still visits every item
+// once.  (Key encode, Llama-2-7B shape: 1.76-1.80 -> 1.65-1.67 ms at RUN 16
+// or 128; value encode 2-4% faster at RUN 128, value decode 1.5% at RUN 16;
+// key decode gains nothing and keeps the identity order.)
+template <int RUN>
+__device__ __forceinline__ int64_t xcd_block() {
+    constexpr int64_t kChunk = 8 * (int64_t)RUN;
+    const int64_t b = blockIdx.x;
+    if (b >= (int64_t)(gridDim.x / kChunk) * kChunk) return b;
+    return (b / kChunk) * kChunk + (b % 8) * RUN + (b / 8) % RUN;
+}
+
 // Full-cache key encode, full groups.  Thread (ti, p) of a block owns channel
 // pair p of key group g0 + ti of one slice, for all G tokens of the group:
 // token t is one dword, and the lanes of a wave read whole token rows (D/2
@@ -275,7 +294,7 @@ encode_k_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int D, int n
     if (ti >= tpb) return;
     const int voff = (ti * G * D + 2 * p) * 2;          // bytes from the batch base
     const int row_bytes = D * 2;
-    for (int64_t batch = blockIdx.x; batch < n_batches; batch += gridDim.x) {
+    for (int64_t batch = xcd_block<16>(); batch < n_batches; batch += gridDim.x) {
         const int64_t s = batch / batches_per_slice;
         const int g0 = (int)(batch - s * batches_per_slice) * tpb;
         const int g = g0 + ti;
@@ -394,7 +413,7 @@ encode_v_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int n_tokens
     const bool cvalid = ALL || c < (D >> 3);
     const bool in_group = ALL || (c / GL) < ngv;
     const int wpt = ngv * G * BITS / 32;
-    for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+    for (int64_t blk = xcd_block<128>(); blk < n_blocks; blk += gridDim.x) {
         const int64_t s = blk / blocks_per_slice;
         const int tb = (int)(blk - s * blocks_per_slice) * rows_per_block;
         const uint16_t* src = in + s * in_stride;
@@ -569,7 +588,7 @@ decode_v_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__
     const int rstep = kBlock >> lpt_log2;
     const int rows_per_block = kRowsPerThread * rstep;
     if (c >= (D >> 3)) return;
-    for (int64_t blk = blockIdx.x; blk < n_blocks; blk += gridDim.x) {
+    for (int64_t blk = xcd_block<16>(); blk < n_blocks; blk += gridDim.x) {
         const int64_t s = blk / blocks_per_slice;
         const int row0 = (int)(blk - s * blocks_per_slice) * rows_per_block;
         if (row0 + rows_per_block <= n_tokens)
