@@ -21,12 +21,12 @@ SOURCES = [os.path.join(CSRC, "kivi_api.cpp"), os.path.join(CSRC, "kivi_kernels.
            os.path.join(CSRC, "kivi_attention.hip"), os.path.join(CSRC, "kivi_copy.hip"),
            os.path.join(CSRC, "kivi_fp8.hip")]
 
+# flags for every compile step; "-shared" goes on the link line only
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # min/max of fp16 values skip NaN quieting (inputs are finite by contract);
     # fp32 division stays correctly rounded (no fast-math flags).
     "-fno-honor-nans",
@@ -36,6 +36,8 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+OBJ_DIR = os.path.join(HERE, "_build")
+
 
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -44,19 +46,43 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libkivi")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into ``libkivi.so`` (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in res.stderr.splitlines()
+def _filtered(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines()
                      if "packed-fp32-ops" not in l and "ignoring feature" not in l)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into ``libkivi.so`` (always recompiles).
+
+    The sources compile in parallel, one hipcc process each (the attention
+    kernels' templates dominate the time), and are linked in one step."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    cc = hipcc()
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
+        cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((cmd, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                                text=True)))
+    failed = []
+    for cmd, obj, proc in jobs:
+        _, err = proc.communicate()
+        err = _filtered(err)
+        if proc.returncode != 0:
+            failed.append(f"{cmd[-3]} ({proc.returncode}):\n{err}")
+        elif verbose and err.strip():
+            print(err, file=sys.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+    tmp = LIB + ".tmp"
+    link = [cc, "--offload-arch=gfx950", "-fPIC", "-shared", *(obj for _, obj, _ in jobs), "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    res = subprocess.run(link, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
-    if verbose and errs.strip():
-        print(errs, file=sys.stderr)
+        raise RuntimeError(f"hipcc link failed ({res.returncode}):\n{_filtered(res.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 
