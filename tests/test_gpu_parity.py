@@ -60,6 +60,24 @@ def test_edge_shapes_with_exact_ties(D, T, G, R, b):
     U.check_round_trip("v", cfg, xv, n)
 
 
+@pytest.mark.parametrize("b", [2, 8])
+def test_xcd_ordered_grids_with_tails(b):
+    """Key encode, value encode and value decode hand each XCD runs of
+    consecutive work items, except in a tail of workgroups past the last whole
+    super-chunk (8 runs), which keeps launch order.  At 23 slices x 3000
+    tokens, D = 128, G = 32 the grids have both parts: key encode 23 x 24 =
+    552 workgroups (runs of 16: 4 super-chunks of 128, tail 40), value encode
+    23 x 47 = 1081 (runs of 128: 1 super-chunk of 1024, tail 57), value
+    decode 1081 (runs of 16: 8 super-chunks, tail 57).  Every output is
+    compared bit for bit, and nothing outside the valid region is written."""
+    S, T, D = 23, 3000, 128
+    x = np.random.default_rng(23 + b).standard_normal((S, T, D)).astype(F16)
+    cfg = K.Config(b, b, 32, 0, D)
+    _log(f"xcd-ordered grids S={S} T={T} b={b}")
+    U.check_round_trip("k", cfg, x, T)
+    U.check_round_trip("v", cfg, x, T)
+
+
 @pytest.mark.parametrize("kind", ["k", "v"])
 @pytest.mark.parametrize("D,G", [(128, 32), (96, 64), (64, 128), (8, 32), (256, 128), (40, 32)])
 def test_strided_input_and_capacity(kind, D, G):
