@@ -131,18 +131,23 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str) -> str:
 
     fs, fetch = read(fetch_csv, "FETCH_SIZE")
     ws, write = read(write_csv, "WRITE_SIZE")
+    # the profiler's output directories, as given on the command line
+    fetch_dir = os.path.dirname(os.path.relpath(fetch_csv, ROOT))
+    write_dir = os.path.dirname(os.path.relpath(write_csv, ROOT))
+    fetch_csv = os.path.relpath(fetch_csv, ROOT)
+    write_csv = os.path.relpath(write_csv, ROOT)
     lines = [
         "# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE; KiB per",
         f"# dispatch, one --pmc pass each) for workload {workload}, each counter scaled by",
         f"# what it reads on the {n_copies} set-up copies of {copy_bytes} bytes each way in the",
         "# same run.  Commands, from the repository root:",
-        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_FETCH_SIZE -o run --output-format csv -- \\",
+        f"#   rocprofv3 --pmc FETCH_SIZE -d {fetch_dir} -o run --output-format csv -- \\",
         f"#       python -u bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline",
-        "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_WRITE_SIZE -o run --output-format csv -- \\",
+        f"#   rocprofv3 --pmc WRITE_SIZE -d {write_dir} -o run --output-format csv -- \\",
         f"#       python -u bench.py --workload {workload} --steps 2 --warmup 1 --no-cpu-baseline",
         f"#   python bench.py --workload {workload} --summarize-traffic \\",
-        "#       gpurun_out/pmc_FETCH_SIZE/run_counter_collection.csv \\",
-        "#       gpurun_out/pmc_WRITE_SIZE/run_counter_collection.csv",
+        f"#       {fetch_csv} \\",
+        f"#       {write_csv}",
         "# bench.py reports these bytes only while kivi_kernels.hip hashes to the value below.",
         f"kernel_source_sha256_16 = {kernel_source_hash()}",
         f"fetch_scale = {fs:.4f}",
