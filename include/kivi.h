@@ -236,7 +236,9 @@ int kivi_decode_v_layers(const kivi_config* cfgs, int64_t n_layers, const int32_
  *   cap_tokens  quantized-token capacity, a multiple of G.
  *   n_quant     tokens quantized so far, a multiple of G, <= cap_tokens.
  *   ring_head   slot of the oldest residual token, in [0, R + G).
- *   ring_count  residual tokens, in [0, R + G - 1] between calls. */
+ *   ring_count  residual tokens, in [0, R + G - 1] between calls.
+ * Every stream call rejects R + G above 2^21 ring slots with KIVI_E_SHAPE
+ * (the kernels address a few slices' rings with 32-bit byte offsets). */
 typedef struct kivi_stream {
     int32_t* k_codes;
     int32_t* v_codes;

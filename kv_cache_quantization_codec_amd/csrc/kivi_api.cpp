@@ -17,6 +17,9 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kMaxTokens = (int64_t(1) << 30);   // per slice, fits int32 math in kernels
+// ring slots (R + G) of a stream: the key flush addresses the rings of up to
+// 2*256/D slices of one block with 32-bit byte offsets (1 KB per slot)
+constexpr int64_t kMaxRingSlots = (int64_t(1) << 21);
 
 bool valid_bits(int32_t b) { return b == 2 || b == 4 || b == 8; }
 bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128; }
@@ -134,7 +137,7 @@ int check_stream(const kivi_config* c, const kivi_stream* s, bool counters) {
     const int64_t G = c->group_size;
     const int64_t slots = int64_t(c->residual_length) + G;
     if (s->cap_tokens < 0 || s->cap_tokens > kMaxTokens || s->cap_tokens % G != 0) return KIVI_E_STATE;
-    if (slots > kMaxTokens) return KIVI_E_SHAPE;
+    if (slots > kMaxRingSlots) return KIVI_E_SHAPE;
     if (counters) {
         if (s->n_quant < 0 || s->n_quant % G != 0 || s->n_quant > s->cap_tokens) return KIVI_E_STATE;
         if (s->ring_head < 0 || s->ring_head >= slots) return KIVI_E_STATE;

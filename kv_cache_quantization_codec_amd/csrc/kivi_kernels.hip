@@ -637,6 +637,103 @@ __device__ __forceinline__ void flush_keys(const StepArgs& a, int tpb, int64_t k
                               a.k_scale, a.k_zero);
 }
 
+// Key flush of the usual step (all G tokens already in the ring, and the
+// group does not wrap around its end), with each channel pair split over a
+// lane pair: lanes 2q and 2q+1 of a slice's D lanes hold channels 2q, 2q+1
+// of tokens [0, G/2) and [G/2, G) of the group, exchange their partial
+// min/max with one DPP step, and each quantizes and packs its own half (a
+// half is a whole number of code words: G/2 is a multiple of 32/b).  Half
+// the registers of the one-lane-per-pair layout, so twice the resident
+// waves, each with half the work: 16,384 slices at G = 32 flush in 45 us
+// instead of 69 us (caches cold), with identical words.
+template <int BITS, int G>
+__device__ __forceinline__ void flush_keys_split(const StepArgs& a, int spb, int64_t kblk) {
+    constexpr int H = G / 2;
+    constexpr int W = G * BITS / 32;
+    constexpr int PER = 32 / BITS;
+    constexpr int HW = W / 2;                   // code words per half group
+    const int D = a.head_dim;
+    const int si = threadIdx.x / D;             // slice within the block
+    const int l = threadIdx.x - si * D;
+    const int q = l >> 1, h = l & 1;            // channel pair, half
+    const int64_t s0 = kblk * spb;
+    const int64_t s = s0 + si;
+    // lanes past the block's slices load slice s0's rows (in bounds) and
+    // stop before storing; every lane takes part in the exchange
+    const bool live = si < spb && s < a.n_slices;
+    const int row_bytes = D * 2;
+    const int64_t nblk = (a.n_slices - s0 < spb) ? a.n_slices - s0 : spb;
+    const __amdgpu_buffer_rsrc_t ring = buffer_rsrc(
+        a.k_ring + s0 * a.ring_slots * (int64_t)D, (uint32_t)(nblk * a.ring_slots * row_bytes));
+    const int voff = ((live ? si : 0) * a.ring_slots * D + 2 * q) * 2 + h * H * row_bytes;
+    uint32_t v[H];
+#pragma unroll
+    for (int i = 0; i < H; ++i)
+        v[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ring, voff, (a.ring_head + i) * row_bytes,
+                                                               kNontemporal);
+    f16x2 mn = as_h2(v[0]), mx = mn;
+#pragma unroll
+    for (int i = 1; i < H; ++i) {
+        mn = pmin(mn, as_h2(v[i]));
+        mx = pmax(mx, as_h2(v[i]));
+    }
+    mn = pmin(mn, as_h2(dpp<0xB1>(as_u32(mn))));       // the partner lane's half
+    mx = pmax(mx, as_h2(dpp<0xB1>(as_u32(mx))));
+    if (!live) return;
+    uint32_t sb0, zb0, sb1, zb1;
+    const QParams p0 = make_params<BITS>((float)mn.x, (float)mx.x, sb0, zb0);
+    const QParams p1 = make_params<BITS>((float)mn.y, (float)mx.y, sb1, zb1);
+    uint32_t w0[HW], w1[HW];
+#pragma unroll
+    for (int w = 0; w < HW; ++w) {
+        w0[w] = 0;
+        w1[w] = 0;
+    }
+    bool redo = !(p0.fast && p1.fast);
+    if (!redo) {
+        float worst = 0.0f;
+#pragma unroll
+        for (int t = 0; t < H; ++t) {
+            const float y0 = __builtin_fmaf(lo_f32(v[t]), p0.rcp, p0.nzr);
+            const float y1 = __builtin_fmaf(hi_f32(v[t]), p1.rcp, p1.nzr);
+            const float r0 = __builtin_rintf(y0);
+            const float r1 = __builtin_rintf(y1);
+            worst = __builtin_fmaxf(worst, __builtin_fmaxf(__builtin_fabsf(y0 - r0),
+                                                           __builtin_fabsf(y1 - r1)));
+            w0[t / PER] |= (uint32_t)r0 << ((t % PER) * BITS);
+            w1[t / PER] |= (uint32_t)r1 << ((t % PER) * BITS);
+        }
+        redo = worst > 0.5f - 0x1p-12f;
+    }
+    if (redo) {
+#pragma unroll
+        for (int w = 0; w < HW; ++w) {
+            w0[w] = 0;
+            w1[w] = 0;
+        }
+#pragma unroll
+        for (int t = 0; t < H; ++t) {
+            const float x0 = lo_f32(v[t]), x1 = hi_f32(v[t]);
+            const uint32_t c0 = p0.fast ? quant_fast<BITS>(x0, p0) : quant_exact<BITS>(x0, p0);
+            const uint32_t c1 = p1.fast ? quant_fast<BITS>(x1, p1) : quant_exact<BITS>(x1, p1);
+            w0[t / PER] |= c0 << ((t % PER) * BITS);
+            w1[t / PER] |= c1 << ((t % PER) * BITS);
+        }
+    }
+    const int out_groups = a.cap_tokens / G;
+    const int64_t grp = s * out_groups + a.n_quant / G;
+    uint32_t* cdst = a.k_codes + grp * (int64_t)(W * D) + h * HW * D + 2 * q;
+#pragma unroll
+    for (int w = 0; w < HW; ++w)
+        __builtin_nontemporal_store(u32x2{w0[w], w1[w]}, reinterpret_cast<u32x2*>(cdst + w * D));
+    if (h == 0) {
+        __builtin_nontemporal_store(sb0 | (sb1 << 16),
+                                    reinterpret_cast<uint32_t*>(a.k_scale + grp * D + 2 * q));
+        __builtin_nontemporal_store(zb0 | (zb1 << 16),
+                                    reinterpret_cast<uint32_t*>(a.k_zero + grp * D + 2 * q));
+    }
+}
+
 // Append of slice s (one token row, 2^lpt_log2 lanes of 8 channels): the new
 // key and value rows go into ring slot (head + count) mod slots, and the
 // value row is quantized at once into store row n_quant + count -- value
@@ -684,6 +781,29 @@ append_flush_kernel(StepArgs a, int tpb, int lpt_log2, int64_t nk, int64_t na) {
             case 2: flush_keys<2, G>(a, tpb, b); break;
             case 4: flush_keys<4, G>(a, tpb, b); break;
             default: flush_keys<8, G>(a, tpb, b); break;
+        }
+        return;
+    }
+    switch (a.v_bits) {
+        case 2: append_row<2, G>(a, b - nk, lpt_log2); break;
+        case 4: append_row<4, G>(a, b - nk, lpt_log2); break;
+        default: append_row<8, G>(a, b - nk, lpt_log2); break;
+    }
+}
+
+// A flush step whose key group lies straight in the ring: block ranges
+// [0, nk) split key flush (spb slices per block), [nk, nk + na) appends.  A
+// kernel of its own, so that the one-lane-per-pair path's registers do not
+// limit these waves.
+template <int G>
+__global__ void __launch_bounds__(kBlock)
+append_flush_split_kernel(StepArgs a, int spb, int lpt_log2, int64_t nk) {
+    const int64_t b = blockIdx.x;
+    if (b < nk) {
+        switch (a.k_bits) {
+            case 2: flush_keys_split<2, G>(a, spb, b); break;
+            case 4: flush_keys_split<4, G>(a, spb, b); break;
+            default: flush_keys_split<8, G>(a, spb, b); break;
         }
         return;
     }
@@ -814,10 +934,19 @@ int run_decode_v(const DecodeArgs& a, hipStream_t st) {
 template <int G>
 int run_append_flush(const StepArgs& a, hipStream_t st) {
     const int D = a.head_dim;
-    const int tpb = key_tiles_per_block(D);
     const int l2 = value_lanes_log2(G, D);
-    const int64_t nk = a.flush ? ceil_div64(a.n_slices, tpb) : 0;
     const int64_t na = ceil_div64(a.n_slices, kBlock >> l2);
+    // the usual flush: all G tokens in the ring, not wrapping around its end
+    if (a.flush && a.ring_count >= G && a.ring_head + G <= a.ring_slots) {
+        const int spb = kBlock / D;
+        const int64_t nk = ceil_div64(a.n_slices, spb);
+        if (nk + na > 0x7FFFFFFF) return (int)hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((append_flush_split_kernel<G>), dim3((unsigned)(nk + na)), dim3(kBlock), 0, st,
+                           a, spb, l2, nk);
+        return (int)hipGetLastError();
+    }
+    const int tpb = key_tiles_per_block(D);
+    const int64_t nk = a.flush ? ceil_div64(a.n_slices, tpb) : 0;
     const int64_t total = nk + na;
     if (total > 0x7FFFFFFF) return (int)hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((append_flush_kernel<G>), dim3((unsigned)total), dim3(kBlock), 0, st, a, tpb,

@@ -167,6 +167,22 @@ def test_stream_state_errors_leave_counters(over, status):
     assert (st.n_quant, st.ring_head, st.ring_count) == before
 
 
+def test_stream_ring_slot_limit():
+    # the flush kernels address a block's rings with 32-bit byte offsets, so
+    # R + G is capped at 2^21 slots for every stream call
+    lib = B.lib()
+    ok = _cfg(G=32, R=(1 << 21) - 32)                     # exactly 2^21 slots
+    st = _stream(ok, S=0, cap=64, ring_count=10)          # no slices: counters only
+    assert _step(ok, st, k=0, v=0) == 0 and st.ring_count == 11
+    big = _cfg(G=32, R=(1 << 21) - 31)
+    for S in (0, 4):
+        st = _stream(big, S=S, ring_count=10)
+        assert _step(big, st) == E["KIVI_E_SHAPE"] and st.ring_count == 10
+    st = _stream(big, S=4, cap=256)
+    assert lib.kivi_stream_prefill(ctypes.byref(big), ctypes.byref(st), FAKE, FAKE, 64, 64 * 128,
+                                   None) == E["KIVI_E_SHAPE"]
+
+
 def test_stream_capacity_error_is_atomic():
     c = _cfg()
     # residual at R tokens: the next append would flush a group into a full store

@@ -71,8 +71,32 @@ CASES = [
 
 @pytest.mark.parametrize("kb,vb,G,R,D,T0,steps", CASES)
 def test_stream_matches_oracle_every_flush(kb, vb, G, R, D, T0, steps):
-    S = 6
-    print(f"stream kb={kb} vb={vb} G={G} R={R} D={D} T0={T0} steps={steps}", flush=True)
+    run_stream(kb, vb, G, R, D, T0, steps, S=6)
+
+
+# Flushes whose key group lies straight in the ring (R >= G, no wrap) split
+# each channel pair over two lanes, D lanes per slice and 256/D slices per
+# block; the others take one lane per pair.  These cases reach the split
+# layout's edges: idle lanes in a block (D = 96), eight slices per wave
+# (D = 8), 64-token halves (G = 128), 4- and 8-bit keys, a ring length that
+# alternates the two layouts (R = 40, G = 32: groups at slots 0, 32, then
+# 64..23 wrapping), and a partial last block (37 slices at D = 96).
+SPLIT_CASES = [
+    # k_bits, v_bits, G, R, D, prefill tokens, steps, slices
+    (4, 2, 32, 64, 96, 100, 120, 6),
+    (8, 4, 128, 128, 64, 300, 300, 6),
+    (2, 8, 32, 40, 8, 50, 150, 6),
+    (2, 2, 32, 32, 96, 70, 100, 37),
+]
+
+
+@pytest.mark.parametrize("kb,vb,G,R,D,T0,steps,S", SPLIT_CASES)
+def test_stream_split_flush_layouts(kb, vb, G, R, D, T0, steps, S):
+    run_stream(kb, vb, G, R, D, T0, steps, S=S)
+
+
+def run_stream(kb, vb, G, R, D, T0, steps, S):
+    print(f"stream kb={kb} vb={vb} G={G} R={R} D={D} T0={T0} steps={steps} S={S}", flush=True)
     sys.stdout.flush()
     rng = np.random.default_rng(kb * 100 + vb * 10 + G + R + D)
     k_all = rng.standard_normal((S, T0 + steps, D)).astype(F16)
