@@ -1,10 +1,13 @@
 """Thin Python binding over libkivi's C ABI (``include/kivi.h``).
 
 Argument marshalling only: every function takes torch tensors that live on
-the GPU, checks that their dtype and strides match the C layouts, and passes
+the GPU, checks that they are device tensors of the expected dtype, layout
+and size (sizes from the library's own sizing entry points), and passes
 ``data_ptr()`` values plus torch's current HIP stream to the entry point of
-the same name.  All codec work runs in the library's HIP kernels; there is no
-fallback of any kind -- importing this module fails loudly when
+the same name.  A tensor that fails a check raises ``ValueError`` before
+the library is called, so no kernel ever sees a host pointer or a buffer
+smaller than its layout.  All codec work runs in the library's HIP kernels;
+there is no fallback of any kind -- importing this module fails loudly when
 ``libkivi.so`` has not been built.
 """
 
@@ -146,13 +149,58 @@ def _check(status: int, what: str):
         raise KiviError(status, what)
 
 
-def _fp16_cache(t: torch.Tensor, D: int, what: str):
-    """(n_slices, slice_stride) of a [S, T, D] fp16 tensor with token stride D."""
+def _on_device(t, what: str, device=None) -> torch.device:
+    """The GPU device of tensor ``t`` (which must equal ``device`` when given)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{what}: expected a torch tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: must be a GPU tensor, got one on {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what}: on {t.device}, but the call's other tensors are on {device}")
+    return t.device
+
+
+def _fp16_cache(t: torch.Tensor, D: int, what: str, n_tokens: int | None = None, device=None):
+    """(n_slices, slice_stride) of a GPU [S, T, D] fp16 tensor with token
+    stride D (and T >= n_tokens when given)."""
+    _on_device(t, what, device)
     if t.dtype != torch.float16 or t.dim() != 3 or t.shape[2] != D:
         raise ValueError(f"{what}: expected float16 [S, T, {D}], got {t.dtype} {tuple(t.shape)}")
     if t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != D):
         raise ValueError(f"{what}: tokens must be contiguous rows of {D} elements")
+    if n_tokens is not None and t.shape[1] < n_tokens:
+        raise ValueError(f"{what}: holds {t.shape[1]} tokens per slice, the call reads or writes {n_tokens}")
     return t.shape[0], t.stride(0)
+
+
+def _sizes(cfg, keys: bool, cap_tokens: int):
+    """(code words, elements of one sidecar) per slice of the key (or value)
+    layouts for ``cap_tokens`` tokens, from the library's sizing entry points."""
+    if keys:
+        words, stats = kivi_k_code_words(cfg, cap_tokens), kivi_k_stat_elems(cfg, cap_tokens)
+    else:
+        words, stats = kivi_v_code_words(cfg, cap_tokens), kivi_v_stat_elems(cfg, cap_tokens)
+    if words < 0 or stats < 0:
+        raise ValueError(f"invalid configuration {cfg} or capacity {cap_tokens}")
+    return words, stats
+
+
+def _payload(cfg, payload, keys: bool, n_slices: int, cap_tokens: int, device, what: str):
+    """Checks a (codes, scale, zero) triple against the C layouts: contiguous
+    GPU tensors on ``device``, int32 / float16, each at least as large as
+    ``n_slices`` slices of the layout for ``cap_tokens`` tokens."""
+    if not isinstance(payload, (tuple, list)) or len(payload) != 3:
+        raise ValueError(f"{what}: expected (codes, scale, zero)")
+    words, stats = _sizes(cfg, keys, cap_tokens)
+    for t, nm, dt, need in ((payload[0], "codes", torch.int32, words),
+                            (payload[1], "scale", torch.float16, stats),
+                            (payload[2], "zero", torch.float16, stats)):
+        _on_device(t, f"{what} {nm}", device)
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{what} {nm}: expected a contiguous {dt} tensor, got {t.dtype}")
+        if t.numel() < n_slices * need:
+            raise ValueError(f"{what} {nm}: {t.numel()} elements, the layout of {n_slices} slices "
+                             f"x {cap_tokens} tokens needs {n_slices * need}")
 
 
 # ---------------------------------------------------------------------------
@@ -181,23 +229,23 @@ def kivi_ring_elems(cfg) -> int:
 
 def alloc_keys(cfg: Config, n_slices: int, cap_tokens: int, device="cuda"):
     """Empty key payload (codes, scale, zero) for ``cap_tokens`` tokens per slice,
-    shaped like the C layouts."""
-    G, D = cfg.group_size, cfg.head_dim
-    ng = -(-cap_tokens // G)
-    W = G * cfg.k_bits // 32
-    codes = torch.empty((n_slices, ng * W, D), dtype=torch.int32, device=device)
-    scale = torch.empty((n_slices, ng, D), dtype=torch.float16, device=device)
-    zero = torch.empty((n_slices, ng, D), dtype=torch.float16, device=device)
+    shaped [S, rows, D] like the C layouts (channel innermost), sized by the
+    library."""
+    words, stats = _sizes(cfg, True, cap_tokens)
+    D = cfg.head_dim
+    codes = torch.empty((n_slices, words // D, D), dtype=torch.int32, device=device)
+    scale = torch.empty((n_slices, stats // D, D), dtype=torch.float16, device=device)
+    zero = torch.empty((n_slices, stats // D, D), dtype=torch.float16, device=device)
     return codes, scale, zero
 
 
 def alloc_values(cfg: Config, n_slices: int, cap_tokens: int, device="cuda"):
-    G, D = cfg.group_size, cfg.head_dim
-    ngv = -(-D // G)
-    W = G * cfg.v_bits // 32
-    codes = torch.empty((n_slices, cap_tokens, ngv * W), dtype=torch.int32, device=device)
-    scale = torch.empty((n_slices, cap_tokens, ngv), dtype=torch.float16, device=device)
-    zero = torch.empty((n_slices, cap_tokens, ngv), dtype=torch.float16, device=device)
+    """Empty value payload shaped [S, cap_tokens, per-row count] like the C
+    layouts (one token row after another), sized by the library."""
+    row_words, row_stats = _sizes(cfg, False, 1)
+    codes = torch.empty((n_slices, cap_tokens, row_words), dtype=torch.int32, device=device)
+    scale = torch.empty((n_slices, cap_tokens, row_stats), dtype=torch.float16, device=device)
+    zero = torch.empty((n_slices, cap_tokens, row_stats), dtype=torch.float16, device=device)
     return codes, scale, zero
 
 
@@ -208,8 +256,9 @@ def alloc_values(cfg: Config, n_slices: int, cap_tokens: int, device="cuda"):
 def kivi_encode_k(cfg, k: torch.Tensor, n_tokens: int, codes, scale, zero,
                   cap_tokens: int | None = None, stream=None):
     """Per-channel key quantization of tokens [0, n_tokens) of ``k`` [S, T, D]."""
-    S, stride = _fp16_cache(k, cfg.head_dim, "k")
+    S, stride = _fp16_cache(k, cfg.head_dim, "k", n_tokens)
     cap = n_tokens if cap_tokens is None else cap_tokens
+    _payload(cfg, (codes, scale, zero), True, S, cap, k.device, "keys")
     _check(lib().kivi_encode_k(_cfg(cfg), _ptr(k), S, n_tokens, stride, cap, _ptr(codes),
                                _ptr(scale), _ptr(zero), _stream_ptr(stream)), "kivi_encode_k")
 
@@ -217,8 +266,9 @@ def kivi_encode_k(cfg, k: torch.Tensor, n_tokens: int, codes, scale, zero,
 def kivi_encode_v(cfg, v: torch.Tensor, n_tokens: int, codes, scale, zero,
                   cap_tokens: int | None = None, stream=None):
     """Per-token value quantization of rows [0, n_tokens) of ``v`` [S, T, D]."""
-    S, stride = _fp16_cache(v, cfg.head_dim, "v")
+    S, stride = _fp16_cache(v, cfg.head_dim, "v", n_tokens)
     cap = n_tokens if cap_tokens is None else cap_tokens
+    _payload(cfg, (codes, scale, zero), False, S, cap, v.device, "values")
     _check(lib().kivi_encode_v(_cfg(cfg), _ptr(v), S, n_tokens, stride, cap, _ptr(codes),
                                _ptr(scale), _ptr(zero), _stream_ptr(stream)), "kivi_encode_v")
 
@@ -226,16 +276,19 @@ def kivi_encode_v(cfg, v: torch.Tensor, n_tokens: int, codes, scale, zero,
 def kivi_decode_k(cfg, codes, scale, zero, n_tokens: int, out: torch.Tensor,
                   cap_tokens: int | None = None, stream=None):
     """Dequantize key tokens [0, n_tokens) into ``out`` [S, >=n_tokens, D]."""
-    S, stride = _fp16_cache(out, cfg.head_dim, "out")
+    S, stride = _fp16_cache(out, cfg.head_dim, "out", n_tokens)
     cap = n_tokens if cap_tokens is None else cap_tokens
+    _payload(cfg, (codes, scale, zero), True, S, cap, out.device, "keys")
     _check(lib().kivi_decode_k(_cfg(cfg), _ptr(codes), _ptr(scale), _ptr(zero), S, n_tokens, cap,
                                _ptr(out), stride, _stream_ptr(stream)), "kivi_decode_k")
 
 
 def kivi_decode_v(cfg, codes, scale, zero, n_tokens: int, out: torch.Tensor,
                   cap_tokens: int | None = None, stream=None):
-    S, stride = _fp16_cache(out, cfg.head_dim, "out")
+    """Dequantize value rows [0, n_tokens) into ``out`` [S, >=n_tokens, D]."""
+    S, stride = _fp16_cache(out, cfg.head_dim, "out", n_tokens)
     cap = n_tokens if cap_tokens is None else cap_tokens
+    _payload(cfg, (codes, scale, zero), False, S, cap, out.device, "values")
     _check(lib().kivi_decode_v(_cfg(cfg), _ptr(codes), _ptr(scale), _ptr(zero), S, n_tokens, cap,
                                _ptr(out), stride, _stream_ptr(stream)), "kivi_decode_v")
 
@@ -280,13 +333,16 @@ def _cfg_array(cfgs):
     return (kivi_config * max(len(cfgs), 1))(*[c.c() if isinstance(c, Config) else c for c in cfgs])
 
 
-def _fp16_layers(t: torch.Tensor, D: int, what: str):
-    """(n_layers, n_slices, layer_stride, slice_stride) of an fp16 [L, S, T, D]
-    tensor with contiguous token rows."""
+def _fp16_layers(t: torch.Tensor, D: int, what: str, n_tokens: int):
+    """(n_layers, n_slices, layer_stride, slice_stride) of a GPU fp16
+    [L, S, T >= n_tokens, D] tensor with contiguous token rows."""
+    _on_device(t, what)
     if t.dtype != torch.float16 or t.dim() != 4 or t.shape[3] != D:
         raise ValueError(f"{what}: expected float16 [L, S, T, {D}], got {t.dtype} {tuple(t.shape)}")
     if t.stride(3) != 1 or (t.shape[2] > 1 and t.stride(2) != D):
         raise ValueError(f"{what}: tokens must be contiguous rows of {D} elements")
+    if t.shape[2] < n_tokens:
+        raise ValueError(f"{what}: holds {t.shape[2]} tokens per slice, the call reads or writes {n_tokens}")
     return t.shape[0], t.shape[1], t.stride(0), t.stride(1)
 
 
@@ -299,10 +355,15 @@ def _layer_ptrs(layers, L: int):
 
 def _coded_layers(name: str, keys: bool, cfgs, x: torch.Tensor, n_tokens: int, layers, cap_tokens,
                   stream):
-    L, S, lstride, sstride = _fp16_layers(x, cfgs[0].head_dim if cfgs else 0, "k" if keys else "v")
+    L, S, lstride, sstride = _fp16_layers(x, cfgs[0].head_dim if cfgs else 0, "k" if keys else "v",
+                                          n_tokens)
     if len(cfgs) != L:
         raise ValueError(f"expected {L} configurations, got {len(cfgs)}")
     cap = n_tokens if cap_tokens is None else cap_tokens
+    if len(layers) != L:
+        raise ValueError(f"expected {L} per-layer payloads, got {len(layers)}")
+    for l in range(L):
+        _payload(cfgs[l], layers[l], keys, S, cap, x.device, f"layer {l}")
     codes, scale, zero = _layer_ptrs(layers, L)
     fn = getattr(lib(), name)
     if name.startswith("kivi_encode"):
@@ -342,17 +403,23 @@ def kivi_decode_v_layers(cfgs, layers, n_tokens: int, out: torch.Tensor, cap_tok
 # ---------------------------------------------------------------------------
 
 class Stream:
-    """Device buffers and host counters of one streaming cache (``kivi_stream``)."""
+    """Device buffers and host counters of one streaming cache (``kivi_stream``).
+
+    ``k_ring`` / ``v_ring`` are fp16 [S, slots, D]; residual token i (0 =
+    the oldest) of every slice sits in slot (ring_head + i) mod slots."""
 
     def __init__(self, cfg: Config, n_slices: int, cap_tokens: int, device="cuda"):
-        G, R, D = cfg.group_size, cfg.residual_length, cfg.head_dim
-        if cap_tokens % G:
+        D = cfg.head_dim
+        if cap_tokens % cfg.group_size:
             raise ValueError("cap_tokens must be a multiple of group_size")
+        ring = kivi_ring_elems(cfg)
+        if ring < 0:
+            raise ValueError(f"invalid configuration {cfg}")
         self.cfg = cfg
         self.keys = alloc_keys(cfg, n_slices, cap_tokens, device)
         self.values = alloc_values(cfg, n_slices, cap_tokens, device)
-        self.k_ring = torch.empty((n_slices, R + G, D), dtype=torch.float16, device=device)
-        self.v_ring = torch.empty((n_slices, R + G, D), dtype=torch.float16, device=device)
+        self.k_ring = torch.empty((n_slices, ring // D, D), dtype=torch.float16, device=device)
+        self.v_ring = torch.empty((n_slices, ring // D, D), dtype=torch.float16, device=device)
         kc, ks, kz = self.keys
         vc, vs, vz = self.values
         self.state = kivi_stream(_ptr(kc), _ptr(vc), _ptr(ks), _ptr(kz), _ptr(vs), _ptr(vz),
@@ -371,16 +438,11 @@ class Stream:
     def ring_count(self) -> int:
         return self.state.ring_count
 
-    def residual(self):
-        """Residual K and V tokens in age order, fp16 [S, count, D] (copies)."""
-        slots = self.k_ring.shape[1]
-        idx = [(self.ring_head + i) % slots for i in range(self.ring_count)]
-        return self.k_ring[:, idx], self.v_ring[:, idx]
-
 
 def kivi_stream_prefill(st: Stream, k: torch.Tensor, v: torch.Tensor, n_tokens: int, stream=None):
-    S, stride = _fp16_cache(k, st.cfg.head_dim, "k")
-    S2, stride2 = _fp16_cache(v, st.cfg.head_dim, "v")
+    dev = st.k_ring.device
+    S, stride = _fp16_cache(k, st.cfg.head_dim, "k", n_tokens, dev)
+    S2, stride2 = _fp16_cache(v, st.cfg.head_dim, "v", n_tokens, dev)
     if S != st.state.n_slices or S2 != S or stride2 != stride:
         raise ValueError("k and v must match the stream's slices and share one stride")
     _check(lib().kivi_stream_prefill(_cfg(st.cfg), ctypes.byref(st.state), _ptr(k), _ptr(v),
@@ -391,6 +453,7 @@ def kivi_append_flush(st: Stream, k_new: torch.Tensor, v_new: torch.Tensor, stre
     """One decode step; returns True when a group was flushed."""
     D = st.cfg.head_dim
     for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _on_device(t, nm, st.k_ring.device)
         if t.dtype != torch.float16 or tuple(t.shape) != (st.state.n_slices, D) or not t.is_contiguous():
             raise ValueError(f"{nm}: expected contiguous float16 [{st.state.n_slices}, {D}]")
     before = st.state.n_quant
@@ -403,18 +466,22 @@ def kivi_append_flush(st: Stream, k_new: torch.Tensor, v_new: torch.Tensor, stre
 # FP8 keys (k8v4 layout)
 # ---------------------------------------------------------------------------
 
-def _rows(t: torch.Tensor, dtype, what: str):
-    """(n_slices, n_rows_allocated, D, slice_stride) of a [S, T, D] tensor with contiguous rows."""
+def _rows(t: torch.Tensor, dtype, what: str, n_tokens: int, device=None):
+    """(n_slices, n_rows_allocated, D, slice_stride) of a GPU [S, T >= n_tokens, D]
+    tensor with contiguous rows."""
+    _on_device(t, what, device)
     if t.dtype != dtype or t.dim() != 3 or t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
         raise ValueError(f"{what}: expected {dtype} [S, T, D] with contiguous token rows")
+    if t.shape[1] < n_tokens:
+        raise ValueError(f"{what}: holds {t.shape[1]} tokens per slice, the call reads or writes {n_tokens}")
     return t.shape[0], t.shape[1], t.shape[2], t.stride(0)
 
 
 def kivi_fp8_encode(k: torch.Tensor, n_tokens: int, out: torch.Tensor, stream=None):
     """FP8 (E4M3) codes of tokens [0, n_tokens) of ``k`` fp16 [S, T, D] into
     ``out`` uint8 [S, T', D]."""
-    S, _, D, si = _rows(k, torch.float16, "k")
-    S2, _, D2, so = _rows(out, torch.uint8, "out")
+    S, _, D, si = _rows(k, torch.float16, "k", n_tokens)
+    S2, _, D2, so = _rows(out, torch.uint8, "out", n_tokens, k.device)
     if (S2, D2) != (S, D):
         raise ValueError("out must match k's slices and head_dim")
     _check(lib().kivi_fp8_encode(_ptr(k), S, n_tokens, D, si, _ptr(out), so, _stream_ptr(stream)),
@@ -422,8 +489,8 @@ def kivi_fp8_encode(k: torch.Tensor, n_tokens: int, out: torch.Tensor, stream=No
 
 
 def kivi_fp8_decode(codes: torch.Tensor, n_tokens: int, out: torch.Tensor, stream=None):
-    S, _, D, si = _rows(codes, torch.uint8, "codes")
-    S2, _, D2, so = _rows(out, torch.float16, "out")
+    S, _, D, si = _rows(codes, torch.uint8, "codes", n_tokens)
+    S2, _, D2, so = _rows(out, torch.float16, "out", n_tokens, codes.device)
     if (S2, D2) != (S, D):
         raise ValueError("out must match the codes' slices and head_dim")
     _check(lib().kivi_fp8_decode(_ptr(codes), S, n_tokens, D, si, _ptr(out), so, _stream_ptr(stream)),
@@ -484,24 +551,34 @@ class AttnCache:
         D = cfg.head_dim
         vc, vs, vz = values
         kc, ks, kz = keys
-        cap = vc.shape[1]
+        dev = _on_device(kc, "key codes")
+        if kc.dim() != 3 or vc.dim() != 3 or vc.shape[0] != kc.shape[0]:
+            raise ValueError("key codes [S, rows, D] and value codes [S, cap_tokens, words per row] "
+                             "expected, with one slice count")
+        S, cap = kc.shape[0], vc.shape[1]
+        _payload(cfg, keys, True, S, cap, dev, "keys")
+        _payload(cfg, values, False, S, cap, dev, "values")
         stride, slots = 0, 0
         if res_k is not None and res_k.shape[1] == 0:     # an empty residual
             res_k = res_v = None
         if res_k is not None:
             for t, nm in ((res_k, "res_k"), (res_v, "res_v")):
+                _on_device(t, nm, dev)
                 if t.dtype != torch.float16 or t.dim() != 3 or t.shape[2] != D or t.stride(2) != 1 \
-                        or (t.shape[1] > 1 and t.stride(1) != D):
-                    raise ValueError(f"{nm}: expected float16 [S, slots, {D}] with contiguous rows")
+                        or (t.shape[1] > 1 and t.stride(1) != D) or t.shape[0] != S:
+                    raise ValueError(f"{nm}: expected float16 [{S}, slots, {D}] with contiguous rows")
             if res_v.stride(0) != res_k.stride(0) or res_v.shape[1] != res_k.shape[1]:
                 raise ValueError("res_k and res_v must share slots and slice stride")
             stride, slots = res_k.stride(0), res_k.shape[1]
         count = slots if res_count is None else res_count
         for t, nm in ((n_quant_per_slice, "n_quant_per_slice"), (res_count_per_slice, "res_count_per_slice")):
-            if t is not None and (t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous()
-                                  or t.shape[0] != kc.shape[0] or t.device.type != "cuda"):
-                raise ValueError(f"{nm}: expected contiguous int32 [n_slices] on the device")
+            if t is not None:
+                _on_device(t, nm, dev)
+                if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.shape[0] != S:
+                    raise ValueError(f"{nm}: expected contiguous int32 [n_slices] on the device")
         self.cfg = cfg
+        self.device = dev
+        self.n_slices = S
         self._refs = (keys, values, res_k, res_v, n_quant_per_slice, res_count_per_slice)
         self.c = kivi_attn_cache(_ptr(kc), _ptr(ks), _ptr(kz), _ptr(vc), _ptr(vs), _ptr(vz),
                                  cap, n_quant, _ptr(res_k), _ptr(res_v), stride, slots,
@@ -518,24 +595,36 @@ def kivi_attention_workspace_bytes(cfg, n_slices: int, q_per_kv: int, n_quant: i
     return lib().kivi_attention_workspace_bytes(_cfg(cfg), n_slices, q_per_kv, n_quant, res_count)
 
 
+def _attention_io(cfg, cache: AttnCache, q: torch.Tensor, out: torch.Tensor):
+    D = cfg.head_dim
+    for t, nm in ((q, "q"), (out, "out")):
+        _on_device(t, nm, cache.device)
+        if t.dtype != torch.float16 or t.dim() != 3 or t.shape[2] != D or not t.is_contiguous():
+            raise ValueError(f"{nm}: expected contiguous float16 [S, q_per_kv, {D}]")
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if q.shape[0] != cache.n_slices:
+        raise ValueError(f"q has {q.shape[0]} slices, the cache {cache.n_slices}")
+    return q.shape[0], q.shape[1]
+
+
 def kivi_decode_attention(cfg, cache: AttnCache, q: torch.Tensor, sm_scale: float,
                           out: torch.Tensor, workspace: torch.Tensor | None = None, stream=None):
     """Attention of ``q`` fp16 [S, q_per_kv, D] over ``cache`` into ``out``
     (same shape).  A workspace of the size the library asks for is allocated
     on ``q``'s device when none is given."""
-    D = cfg.head_dim
-    for t, nm in ((q, "q"), (out, "out")):
-        if t.dtype != torch.float16 or t.dim() != 3 or t.shape[2] != D or not t.is_contiguous():
-            raise ValueError(f"{nm}: expected contiguous float16 [S, q_per_kv, {D}]")
-    if out.shape != q.shape:
-        raise ValueError("out must have q's shape")
-    S, r = q.shape[0], q.shape[1]
+    S, r = _attention_io(cfg, cache, q, out)
     need = kivi_attention_workspace_bytes(cfg, S, r, cache.c.n_quant, cache.c.res_count)
     if need < 0:
         raise KiviError(-6, "kivi_attention_workspace_bytes")
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _on_device(workspace, "workspace", q.device)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace: expected a contiguous tensor")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().kivi_decode_attention(_cfg(cfg), ctypes.byref(cache.c), S, r, _ptr(q),
                                        float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
                                        _stream_ptr(stream)), "kivi_decode_attention")
+

@@ -35,6 +35,14 @@ def is_poison(a: np.ndarray) -> bool:
     return bool(np.all(a == np.uint16(POISON16)))
 
 
+def ring_residual(st):
+    """Residual K and V tokens of a ``K.Stream`` in age order, fp16 [S, count, D]
+    copies: residual token i sits in ring slot (ring_head + i) mod slots."""
+    slots = st.k_ring.shape[1]
+    idx = [(st.ring_head + i) % slots for i in range(st.ring_count)]
+    return st.k_ring[:, idx], st.v_ring[:, idx]
+
+
 def assert_equal(name, got: np.ndarray, want: np.ndarray):
     if got.shape != want.shape:
         raise AssertionError(f"{name}: shape {got.shape} != {want.shape}")

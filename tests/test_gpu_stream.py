@@ -43,7 +43,7 @@ def compare_stream(st: K.Stream, sr: ref.StreamRef, slices=None, group_range=Non
         U.assert_equal("stream value codes", U.words(vc[sel][:, r0:r1]), pc.view(np.uint32)[:, r0:r1])
         U.assert_equal("stream value scale", U.bits16(vs[sel][:, r0:r1]), ps.view(np.uint16)[:, r0:r1])
         U.assert_equal("stream value zero", U.bits16(vz[sel][:, r0:r1]), pz.view(np.uint16)[:, r0:r1])
-    rk, rv = st.residual()
+    rk, rv = U.ring_residual(st)
     U.assert_equal("residual k", U.bits16(rk[sel]), sr.res_k.view(np.uint16))
     U.assert_equal("residual v", U.bits16(rv[sel]), sr.res_v.view(np.uint16))
     # value rows are quantized on arrival: the residual's rows (below the
