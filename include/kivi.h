@@ -51,7 +51,9 @@
  * hip_stream (a hipStream_t; NULL means the default stream), so outputs are
  * ready when that stream reaches the enqueued work.  Calls on different
  * streams are independent and re-entrant; the library's only global state
- * is the thread-local code of the last failed HIP launch.
+ * is the thread-local code of the last failed HIP launch, plus the static
+ * device scratch of kivi_decode_attention_noalloc (and its address per
+ * device), which only that entry point uses.
  *
  * Errors.  Every entry point returns KIVI_OK (0) or a negative KIVI_E_*
  * code.  Argument checks all run before any HIP call, so a non-zero return
@@ -98,7 +100,8 @@ enum {
     KIVI_E_ALIGN = -7,      /* pointer not 16-byte aligned or stride not a multiple of 8 */
     KIVI_E_CAPACITY = -8,   /* streaming flush would pass cap_tokens */
     KIVI_E_STATE = -9,      /* kivi_stream counters inconsistent */
-    KIVI_E_HIP = -10        /* a HIP launch failed; see kivi_last_hip_error() */
+    KIVI_E_HIP = -10,       /* a HIP launch failed; see kivi_last_hip_error() */
+    KIVI_E_SCRATCH = -11    /* the call needs more than the library's static scratch */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -419,6 +422,31 @@ int kivi_decode_attention(const kivi_config* cfg, const kivi_attn_cache* cache,
                           int64_t n_slices, int32_t q_per_kv, const void* q_fp16,
                           float sm_scale, void* out_fp16, void* workspace,
                           int64_t workspace_bytes, void* hip_stream);
+
+/* Size in bytes of the static attention scratch that libkivi holds on each
+ * device it runs kivi_decode_attention_noalloc on (from that device's first
+ * such call until the process ends). */
+#define KIVI_ATTENTION_SCRATCH_BYTES (128LL << 20)
+
+/* kivi_decode_attention for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, kernels and results (bit for bit) as
+ * kivi_decode_attention, without the workspace: when the call splits slices
+ * (kivi_attention_workspace_bytes(...) > 0) its partial sums go to a
+ * library-owned static device buffer of KIVI_ATTENTION_SCRATCH_BYTES bytes
+ * per device, and a call that would need more returns KIVI_E_SCRATCH with
+ * nothing enqueued (split the slices over several calls).  Nothing is
+ * allocated or freed, by the library or by any routine it calls.  The device
+ * is the one hip_stream belongs to (the current device for NULL); the first
+ * call on a device looks up that device's buffer address once (no
+ * allocation; make that first call outside graph capture).  Every call on
+ * one device shares its buffer and leaves the last call's partials in it:
+ * calls that overlap on one device (concurrent streams, or threads) race and
+ * must be ordered by the caller.  The buffer needs no clearing: every
+ * partial is written before it is read. */
+int kivi_decode_attention_noalloc(const kivi_config* cfg, const kivi_attn_cache* cache,
+                                  int64_t n_slices, int32_t q_per_kv, const void* q_fp16,
+                                  float sm_scale, void* out_fp16, void* hip_stream);
 
 #ifdef __cplusplus
 }

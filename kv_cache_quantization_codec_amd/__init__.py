@@ -6,6 +6,7 @@ over it.
 """
 
 from .binding import (  # noqa: E402,F401
+    ATTENTION_SCRATCH_BYTES,
     AttnCache,
     Config,
     KiviError,
@@ -17,6 +18,7 @@ from .binding import (  # noqa: E402,F401
     kivi_attention_workspace_bytes,
     kivi_boundary_layers,
     kivi_decode_attention,
+    kivi_decode_attention_noalloc,
     kivi_decode_k,
     kivi_decode_k_layers,
     kivi_decode_v,

@@ -25,8 +25,11 @@ KIVI_OK = 0
 STATUS_NAMES = {
     0: "KIVI_OK", -1: "KIVI_E_NULL", -2: "KIVI_E_BITS", -3: "KIVI_E_GROUP",
     -4: "KIVI_E_HEAD_DIM", -5: "KIVI_E_RESIDUAL", -6: "KIVI_E_SHAPE", -7: "KIVI_E_ALIGN",
-    -8: "KIVI_E_CAPACITY", -9: "KIVI_E_STATE", -10: "KIVI_E_HIP",
+    -8: "KIVI_E_CAPACITY", -9: "KIVI_E_STATE", -10: "KIVI_E_HIP", -11: "KIVI_E_SCRATCH",
 }
+
+# bytes of the library's static attention scratch per device (KIVI_ATTENTION_SCRATCH_BYTES)
+ATTENTION_SCRATCH_BYTES = 128 << 20
 
 
 class KiviError(RuntimeError):
@@ -94,6 +97,7 @@ SIGNATURES = [
     ("kivi_stream_restore", _I32, [_CFG, _ST, _P, _I64, _I64, _I64, _I64, _P]),
     ("kivi_attention_workspace_bytes", _I64, [_CFG, _I64, _I32, _I64, _I64]),
     ("kivi_decode_attention", _I32, [_CFG, _AC, _I64, _I32, _P, ctypes.c_float, _P, _P, _I64, _P]),
+    ("kivi_decode_attention_noalloc", _I32, [_CFG, _AC, _I64, _I32, _P, ctypes.c_float, _P, _P]),
 ]
 
 _lib = None
@@ -628,3 +632,13 @@ def kivi_decode_attention(cfg, cache: AttnCache, q: torch.Tensor, sm_scale: floa
                                        float(sm_scale), _ptr(out), _ptr(workspace), ws_bytes,
                                        _stream_ptr(stream)), "kivi_decode_attention")
 
+
+def kivi_decode_attention_noalloc(cfg, cache: AttnCache, q: torch.Tensor, sm_scale: float,
+                                  out: torch.Tensor, stream=None):
+    """:func:`kivi_decode_attention` with the split partials in the library's
+    static per-device scratch (``ATTENTION_SCRATCH_BYTES``): allocates
+    nothing.  Calls that overlap on one device race on that scratch."""
+    S, r = _attention_io(cfg, cache, q, out)
+    _check(lib().kivi_decode_attention_noalloc(_cfg(cfg), ctypes.byref(cache.c), S, r, _ptr(q),
+                                               float(sm_scale), _ptr(out), _stream_ptr(stream)),
+           "kivi_decode_attention_noalloc")

@@ -216,6 +216,100 @@ int64_t attention_ws_bytes(const kivi_config* c, int64_t n_slices, int32_t q_per
     return total;
 }
 
+// Decode attention, with the caller's workspace or (static_scratch) the
+// library's per-device static buffer for the split partials.  Every check
+// runs before the first HIP call; the static buffer's address is looked up
+// only when the call needs it.
+int attention_call(const kivi_config* cfg, const kivi_attn_cache* cache, int64_t n_slices,
+                   int32_t q_per_kv, const void* q, float sm_scale, void* out, void* workspace,
+                   int64_t workspace_bytes, bool static_scratch, void* stream) {
+    int s = check_attention_config(cfg, q_per_kv);
+    if (s) return s;
+    if (!cache) return KIVI_E_NULL;
+    const kivi_attn_cache& c = *cache;
+    const int64_t D = cfg->head_dim;
+    if (n_slices < 0) return KIVI_E_SHAPE;
+    if (c.cap_tokens < 0 || c.cap_tokens > kMaxTokens || c.n_quant < 0 || c.n_quant > c.cap_tokens)
+        return KIVI_E_SHAPE;
+    if (c.res_count < 0 || c.res_slots < c.res_count || c.res_slots > kMaxTokens) return KIVI_E_SHAPE;
+    if (c.res_count > 0 && (c.res_head < 0 || c.res_head >= c.res_slots)) return KIVI_E_SHAPE;
+    if (!__builtin_isfinite(sm_scale)) return KIVI_E_SHAPE;
+    if (n_slices == 0) return KIVI_OK;
+    if (c.n_quant + c.res_count < 1) return KIVI_E_SHAPE;
+    if ((c.n_quant_per_slice && (reinterpret_cast<uintptr_t>(c.n_quant_per_slice) & 3u)) ||
+        (c.res_count_per_slice && (reinterpret_cast<uintptr_t>(c.res_count_per_slice) & 3u)))
+        return KIVI_E_ALIGN;
+    const kivi::AttnPlan plan = kivi::attn_plan(n_slices, c.n_quant, c.res_count);
+    int64_t groups = 0;
+    if (!mul_ok(n_slices, plan.n_splits, &groups) || groups > INT32_MAX) return KIVI_E_SHAPE;
+    int64_t tmp = 0;
+    if (!mul_ok(n_slices, (int64_t)q_per_kv * D * 2, &tmp)) return KIVI_E_SHAPE;
+    if (c.n_quant > 0) {
+        if (!mul_ok(n_slices, k_words(cfg, c.cap_tokens) * 4, &tmp) ||
+            !mul_ok(n_slices, v_words(cfg, c.cap_tokens) * 4, &tmp))
+            return KIVI_E_SHAPE;
+    }
+    if (c.res_count > 0) {
+        if (c.res_slice_stride % 8 != 0) return KIVI_E_ALIGN;
+        if (!mul_ok(c.res_slots, D, &tmp) || c.res_slice_stride < tmp) return KIVI_E_SHAPE;
+        if (!mul_ok(n_slices, c.res_slice_stride, &tmp)) return KIVI_E_SHAPE;
+    }
+    const int64_t need = attention_ws_bytes(cfg, n_slices, q_per_kv, plan);
+    if (need < 0) return KIVI_E_SHAPE;
+    if (static_scratch) {
+        if (need > KIVI_ATTENTION_SCRATCH_BYTES) return KIVI_E_SCRATCH;
+    } else if (workspace_bytes < need) {
+        return KIVI_E_SHAPE;
+    }
+    if (!q || !out) return KIVI_E_NULL;
+    if (c.n_quant > 0 && (!c.k_codes || !c.k_scale || !c.k_zero || !c.v_codes || !c.v_scale || !c.v_zero))
+        return KIVI_E_NULL;
+    if (c.res_count > 0 && (!c.res_k || !c.res_v)) return KIVI_E_NULL;
+    if (!static_scratch && need > 0 && !workspace) return KIVI_E_NULL;
+    if (!aligned16(q) || !aligned16(out) || (!static_scratch && need > 0 && !aligned16(workspace)))
+        return KIVI_E_ALIGN;
+    if (c.n_quant > 0 && (!aligned16(c.k_codes) || !aligned16(c.k_scale) || !aligned16(c.k_zero) ||
+                          !aligned16(c.v_codes) || !aligned16(c.v_scale) || !aligned16(c.v_zero)))
+        return KIVI_E_ALIGN;
+    if (c.res_count > 0 && (!aligned16(c.res_k) || !aligned16(c.res_v))) return KIVI_E_ALIGN;
+    if (static_scratch && need > 0) {
+        // all checks passed: the first HIP call (the buffer of the stream's device)
+        s = record(kivi::attention_scratch(stream, &workspace));
+        if (s) return s;
+    }
+
+    kivi::AttnArgs a;
+    a.k_codes = reinterpret_cast<const uint32_t*>(c.k_codes);
+    a.k_scale = static_cast<const uint16_t*>(c.k_scale);
+    a.k_zero = static_cast<const uint16_t*>(c.k_zero);
+    a.v_codes = reinterpret_cast<const uint32_t*>(c.v_codes);
+    a.v_scale = static_cast<const uint16_t*>(c.v_scale);
+    a.v_zero = static_cast<const uint16_t*>(c.v_zero);
+    a.res_k = static_cast<const uint16_t*>(c.res_k);
+    a.res_v = static_cast<const uint16_t*>(c.res_v);
+    a.n_quant_s = c.n_quant > 0 ? c.n_quant_per_slice : nullptr;
+    a.res_count_s = c.res_count > 0 ? c.res_count_per_slice : nullptr;
+    a.q = static_cast<const uint16_t*>(q);
+    a.out = static_cast<uint16_t*>(out);
+    a.ws_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
+    a.ws_o = need > 0 ? static_cast<float*>(workspace) + n_slices * plan.n_splits * q_per_kv * 2 : nullptr;
+    a.n_slices = n_slices;
+    a.res_stride = c.res_slice_stride;
+    a.cap_tokens = static_cast<int32_t>(c.cap_tokens);
+    a.n_quant = static_cast<int32_t>(c.n_quant);
+    a.res_slots = static_cast<int32_t>(c.res_slots);
+    a.res_head = static_cast<int32_t>(c.res_count > 0 ? c.res_head : 0);
+    a.res_count = static_cast<int32_t>(c.res_count);
+    a.head_dim = cfg->head_dim;
+    a.group_size = cfg->group_size;
+    a.k_bits = cfg->k_bits;
+    a.v_bits = cfg->v_bits;
+    a.q_per_kv = q_per_kv;
+    a.logit_scale = sm_scale * 1.4426950408889634f;
+    a.plan = plan;
+    return record(kivi::launch_attention(a, stream));
+}
+
 // ---- layer-wise coding of a model with per-layer configurations ----
 
 uintptr_t addr(const void* p) { return reinterpret_cast<uintptr_t>(p); }
@@ -310,6 +404,8 @@ const char* kivi_status_string(int status) {
         case KIVI_E_CAPACITY: return "KIVI_E_CAPACITY: the quantized store is full";
         case KIVI_E_STATE: return "KIVI_E_STATE: inconsistent stream counters";
         case KIVI_E_HIP: return "KIVI_E_HIP: a HIP launch failed";
+        case KIVI_E_SCRATCH:
+            return "KIVI_E_SCRATCH: the call needs more than KIVI_ATTENTION_SCRATCH_BYTES of partial sums";
         default: return "unknown kivi status";
     }
 }
@@ -528,80 +624,14 @@ int64_t kivi_attention_workspace_bytes(const kivi_config* cfg, int64_t n_slices,
 int kivi_decode_attention(const kivi_config* cfg, const kivi_attn_cache* cache, int64_t n_slices,
                           int32_t q_per_kv, const void* q, float sm_scale, void* out,
                           void* workspace, int64_t workspace_bytes, void* stream) {
-    int s = check_attention_config(cfg, q_per_kv);
-    if (s) return s;
-    if (!cache) return KIVI_E_NULL;
-    const kivi_attn_cache& c = *cache;
-    const int64_t D = cfg->head_dim;
-    if (n_slices < 0) return KIVI_E_SHAPE;
-    if (c.cap_tokens < 0 || c.cap_tokens > kMaxTokens || c.n_quant < 0 || c.n_quant > c.cap_tokens)
-        return KIVI_E_SHAPE;
-    if (c.res_count < 0 || c.res_slots < c.res_count || c.res_slots > kMaxTokens) return KIVI_E_SHAPE;
-    if (c.res_count > 0 && (c.res_head < 0 || c.res_head >= c.res_slots)) return KIVI_E_SHAPE;
-    if (!__builtin_isfinite(sm_scale)) return KIVI_E_SHAPE;
-    if (n_slices == 0) return KIVI_OK;
-    if (c.n_quant + c.res_count < 1) return KIVI_E_SHAPE;
-    if ((c.n_quant_per_slice && (reinterpret_cast<uintptr_t>(c.n_quant_per_slice) & 3u)) ||
-        (c.res_count_per_slice && (reinterpret_cast<uintptr_t>(c.res_count_per_slice) & 3u)))
-        return KIVI_E_ALIGN;
-    const kivi::AttnPlan plan = kivi::attn_plan(n_slices, c.n_quant, c.res_count);
-    int64_t groups = 0;
-    if (!mul_ok(n_slices, plan.n_splits, &groups) || groups > INT32_MAX) return KIVI_E_SHAPE;
-    int64_t tmp = 0;
-    if (!mul_ok(n_slices, (int64_t)q_per_kv * D * 2, &tmp)) return KIVI_E_SHAPE;
-    if (c.n_quant > 0) {
-        if (!mul_ok(n_slices, k_words(cfg, c.cap_tokens) * 4, &tmp) ||
-            !mul_ok(n_slices, v_words(cfg, c.cap_tokens) * 4, &tmp))
-            return KIVI_E_SHAPE;
-    }
-    if (c.res_count > 0) {
-        if (c.res_slice_stride % 8 != 0) return KIVI_E_ALIGN;
-        if (!mul_ok(c.res_slots, D, &tmp) || c.res_slice_stride < tmp) return KIVI_E_SHAPE;
-        if (!mul_ok(n_slices, c.res_slice_stride, &tmp)) return KIVI_E_SHAPE;
-    }
-    const int64_t need = attention_ws_bytes(cfg, n_slices, q_per_kv, plan);
-    if (need < 0 || workspace_bytes < need) return KIVI_E_SHAPE;
-    if (!q || !out) return KIVI_E_NULL;
-    if (c.n_quant > 0 && (!c.k_codes || !c.k_scale || !c.k_zero || !c.v_codes || !c.v_scale || !c.v_zero))
-        return KIVI_E_NULL;
-    if (c.res_count > 0 && (!c.res_k || !c.res_v)) return KIVI_E_NULL;
-    if (need > 0 && !workspace) return KIVI_E_NULL;
-    if (!aligned16(q) || !aligned16(out) || (need > 0 && !aligned16(workspace))) return KIVI_E_ALIGN;
-    if (c.n_quant > 0 && (!aligned16(c.k_codes) || !aligned16(c.k_scale) || !aligned16(c.k_zero) ||
-                          !aligned16(c.v_codes) || !aligned16(c.v_scale) || !aligned16(c.v_zero)))
-        return KIVI_E_ALIGN;
-    if (c.res_count > 0 && (!aligned16(c.res_k) || !aligned16(c.res_v))) return KIVI_E_ALIGN;
+    return attention_call(cfg, cache, n_slices, q_per_kv, q, sm_scale, out, workspace, workspace_bytes,
+                          false, stream);
+}
 
-    kivi::AttnArgs a;
-    a.k_codes = reinterpret_cast<const uint32_t*>(c.k_codes);
-    a.k_scale = static_cast<const uint16_t*>(c.k_scale);
-    a.k_zero = static_cast<const uint16_t*>(c.k_zero);
-    a.v_codes = reinterpret_cast<const uint32_t*>(c.v_codes);
-    a.v_scale = static_cast<const uint16_t*>(c.v_scale);
-    a.v_zero = static_cast<const uint16_t*>(c.v_zero);
-    a.res_k = static_cast<const uint16_t*>(c.res_k);
-    a.res_v = static_cast<const uint16_t*>(c.res_v);
-    a.n_quant_s = c.n_quant > 0 ? c.n_quant_per_slice : nullptr;
-    a.res_count_s = c.res_count > 0 ? c.res_count_per_slice : nullptr;
-    a.q = static_cast<const uint16_t*>(q);
-    a.out = static_cast<uint16_t*>(out);
-    a.ws_ml = need > 0 ? static_cast<float*>(workspace) : nullptr;
-    a.ws_o = need > 0 ? static_cast<float*>(workspace) + n_slices * plan.n_splits * q_per_kv * 2 : nullptr;
-    a.n_slices = n_slices;
-    a.res_stride = c.res_slice_stride;
-    a.cap_tokens = static_cast<int32_t>(c.cap_tokens);
-    a.n_quant = static_cast<int32_t>(c.n_quant);
-    a.res_slots = static_cast<int32_t>(c.res_slots);
-    a.res_head = static_cast<int32_t>(c.res_count > 0 ? c.res_head : 0);
-    a.res_count = static_cast<int32_t>(c.res_count);
-    a.head_dim = cfg->head_dim;
-    a.group_size = cfg->group_size;
-    a.k_bits = cfg->k_bits;
-    a.v_bits = cfg->v_bits;
-    a.q_per_kv = q_per_kv;
-    a.logit_scale = sm_scale * 1.4426950408889634f;
-    a.plan = plan;
-    return record(kivi::launch_attention(a, stream));
+int kivi_decode_attention_noalloc(const kivi_config* cfg, const kivi_attn_cache* cache, int64_t n_slices,
+                                  int32_t q_per_kv, const void* q, float sm_scale, void* out,
+                                  void* stream) {
+    return attention_call(cfg, cache, n_slices, q_per_kv, q, sm_scale, out, nullptr, 0, true, stream);
 }
 
 int64_t kivi_stream_image_bytes(const kivi_config* cfg, int64_t n_slices, int64_t n_quant) {

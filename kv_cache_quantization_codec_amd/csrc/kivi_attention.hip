@@ -42,6 +42,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
+#include "../../include/kivi.h"
 #include "kivi_launch.h"
 
 namespace kivi {
@@ -707,7 +711,47 @@ int run_attention(const AttnArgs& a, hipStream_t st) {
     return (int)e;
 }
 
+// The split partials of kivi_decode_attention_noalloc: a static buffer of
+// each device (held until the process ends), so that entry point allocates
+// nothing.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels get the per-device address from attention_scratch.
+__device__ __align__(256) float scratch[KIVI_ATTENTION_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
 }  // namespace
+
+int attention_scratch(void* stream, void** ptr) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return (int)e;
+    int dev = cur;
+    if (stream) {
+        e = hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dev);
+        if (e != hipSuccess) return (int)e;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            // once per device, with that device current
+            if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return (int)e;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (dev != cur) {
+                const hipError_t back = hipSetDevice(cur);
+                if (e == hipSuccess) e = back;
+            }
+            if (e != hipSuccess || !p) return (int)(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return (int)hipSuccess;
+}
 
 int launch_attention(const AttnArgs& a, void* stream) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -156,6 +156,10 @@ int launch_decode_v(const DecodeArgs& a, void* stream);
 int launch_append_flush(const StepArgs& a, void* stream);
 int launch_ring_fill(const RingFillArgs& a, void* stream);
 int launch_attention(const AttnArgs& a, void* stream);
+// Device address of the static attention scratch (KIVI_ATTENTION_SCRATCH_BYTES
+// bytes) on the device that `stream` belongs to (the current device for a
+// null stream), looked up once per device; returns a hipError_t value.
+int attention_scratch(void* stream, void** ptr);
 int launch_fp8_encode(const Fp8Args& a, void* stream);
 int launch_fp8_decode(const Fp8Args& a, void* stream);
 // height rows of width bytes, between any mix of host and device memory

@@ -64,7 +64,7 @@ def test_head_dim_limits(D, status):
     assert (_ws(c, 4, 1, 64, 8) >= 0) == (status == "KIVI_OK")
 
 
-@pytest.mark.parametrize("over,kw,status", [
+ARGUMENT_ERRORS = [
     ({}, {"r": 0}, "KIVI_E_SHAPE"),
     ({}, {"r": 9}, "KIVI_E_SHAPE"),
     ({}, {"S": -1}, "KIVI_E_SHAPE"),
@@ -91,7 +91,10 @@ def test_head_dim_limits(D, status):
     ({"res_k": FAKE + 8}, {}, "KIVI_E_ALIGN"),
     ({"n_quant_per_slice": FAKE + 2}, {}, "KIVI_E_ALIGN"),
     ({"res_count_per_slice": FAKE + 1}, {}, "KIVI_E_ALIGN"),
-])
+]
+
+
+@pytest.mark.parametrize("over,kw,status", ARGUMENT_ERRORS)
 def test_argument_errors(over, kw, status):
     c = _cfg()
     assert _ws(c, 4, 2, 200, 40) > 0, "the reference call must need a workspace"
@@ -119,3 +122,42 @@ def test_no_slices_is_a_noop_after_config_checks():
     c = _cfg()
     assert _call(c, _cache(), S=0, q=0, out=0, ws=0, ws_bytes=0) == E["KIVI_OK"]
     assert _call(_cfg(kb=3), _cache(), S=0) == E["KIVI_E_BITS"]
+
+
+# ---- the no-allocation variant (library-owned static scratch) ----
+
+def _call_noalloc(c, cache, S=4, r=2, q=FAKE, sm=0.125, out=FAKE):
+    return B.lib().kivi_decode_attention_noalloc(ctypes.byref(c) if c else None,
+                                                 ctypes.byref(cache) if cache else None,
+                                                 S, r, q, sm, out, None)
+
+
+@pytest.mark.parametrize("over,kw,status", [e for e in ARGUMENT_ERRORS if not set(e[1]) & {"ws", "ws_bytes"}])
+def test_noalloc_argument_errors_match(over, kw, status):
+    c = _cfg()
+    assert _call_noalloc(c, _cache(**over), **kw) == E[status]
+
+
+def test_noalloc_rejects_calls_beyond_the_scratch():
+    c = _cfg()
+    # 8192 slices x 8 query heads x 16256 quantized tokens: 4 splits of
+    # (max, sum, 128 outputs) fp32 per head = 136,314,880 bytes > 128 MiB
+    cache = _cache(cap_tokens=16384, n_quant=16256, res_k=0, res_v=0, res_count=0, res_slots=0,
+                   res_head=0, res_slice_stride=0)
+    need = _ws(c, 8192, 8, 16256, 0)
+    assert need == 8192 * 4 * 8 * 130 * 4 > B.ATTENTION_SCRATCH_BYTES
+    assert _call_noalloc(c, cache, S=8192, r=8) == E["KIVI_E_SCRATCH"]
+    assert B.lib().kivi_status_string(E["KIVI_E_SCRATCH"]).decode().startswith("KIVI_E_SCRATCH")
+    # config and cache checks come first, as in kivi_decode_attention
+    assert _call_noalloc(None, cache, S=8192, r=8) == E["KIVI_E_NULL"]
+    assert _call_noalloc(c, None) == E["KIVI_E_NULL"]
+    assert _call_noalloc(c, _cache(), S=0, q=0, out=0) == E["KIVI_OK"]
+
+
+def test_scratch_size_matches_header():
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "include", "kivi.h")).read()
+    m = re.search(r"#define KIVI_ATTENTION_SCRATCH_BYTES \((\d+)LL << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.ATTENTION_SCRATCH_BYTES

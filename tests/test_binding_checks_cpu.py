@@ -175,7 +175,7 @@ def test_attention_cache_and_queries_are_checked(host_as_device):
     with pytest.raises(ValueError, match="slices"):
         K.kivi_decode_attention(CFG, cache, _fp16(S + 1, 2, D), 0.1, _fp16(S + 1, 2, D))
     with pytest.raises(ValueError, match="shape"):
-        K.kivi_decode_attention(CFG, cache, q, 0.1, _fp16(S, 1, D))
+        K.kivi_decode_attention_noalloc(CFG, cache, q, 0.1, _fp16(S, 1, D))
     with pytest.raises(ValueError, match="res_k"):
         K.AttnCache(CFG, keys, vals, N, _fp16(S + 1, 8, D), _fp16(S + 1, 8, D))
 
