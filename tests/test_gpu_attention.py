@@ -32,6 +32,7 @@ import torch
 import kv_cache_quantization_codec_amd as K
 from oracle import attention_ref as att
 from oracle import kivi_ref as ref
+from tests.gpu_util import attention_bound as _bound
 
 pytestmark = pytest.mark.gpu
 
@@ -83,40 +84,6 @@ def _ring_dev(res_k, res_v, slots, head):
         rk[:, idx] = res_k.view(np.uint16)
         rv[:, idx] = res_v.view(np.uint16)
     return _to_dev(rk.view(F16), torch.float16), _to_dev(rv.view(F16), torch.float16)
-
-
-def _bound(q, kp, vp, n, res_k, res_v, kb, vb, G, sm_scale, want, n_splits):
-    """Elementwise tolerance [S, r, D] of the module docstring."""
-    q64 = q.astype(np.float64)
-    S, r, D = q.shape
-    parts_a, parts_mv, parts_mvz = [], [], []
-    if n:
-        kd = att.dequantize_exact_k(*kp, n, kb, G)
-        kz = np.asarray(kp[2]).astype(np.float64)[:, np.arange(n) // G, :]
-        A = np.einsum("srd,std->srt", np.abs(q64), np.abs(kd) + 2 * np.abs(kz))
-        vd = att.dequantize_exact_v(*vp, n, vb, G, D)
-        vz = np.asarray(vp[2]).astype(np.float64)[:, :n, :][:, :, np.arange(D) // G]
-        parts_a.append(A)
-        parts_mv.append(np.abs(vd))
-        parts_mvz.append(np.abs(vd) + 2 * np.abs(vz))
-    if res_k.shape[1]:
-        rk, rv = res_k.astype(np.float64), res_v.astype(np.float64)
-        parts_a.append(np.einsum("srd,std->srt", np.abs(q64), np.abs(rk)))
-        parts_mv.append(np.abs(rv))
-        parts_mvz.append(np.abs(rv))
-    A = np.concatenate(parts_a, axis=2)                     # [S, r, T]
-    kk, _ = att.cache_tokens(kp, vp, n, res_k, res_v, kb, vb, G, D)
-    logits = np.einsum("srd,std->srt", q64, kk) * sm_scale
-    T = A.shape[2]
-    delta = sm_scale * ((D + 2) * U + 2.0 ** -21) * A + 3 * U * np.abs(logits)
-    spread = (logits.max(axis=2, keepdims=True) - logits) / np.log(2)
-    eps = (delta.max(axis=2) + 2.0 ** -22 + U * spread.max(axis=2)
-           + (-(-T // 32)) * 2.0 ** -21 + (n_splits + 2) * 2.0 ** -22)        # [S, r]
-    mv = np.concatenate(parts_mv, axis=1).max(axis=1)       # [S, D]
-    mvz = np.concatenate(parts_mvz, axis=1).max(axis=1)
-    return (2.0 ** -11 * np.abs(want) + 2.0 ** -25
-            + 2.1 * eps[:, :, None] * mv[:, None, :]
-            + ((T + 8) * U + 2.0 ** -21) * mvz[:, None, :])
 
 
 def _gen(seed, S, n, n_res, D, r, outliers=True):

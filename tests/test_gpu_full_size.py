@@ -1,9 +1,12 @@
 """The full-size workloads, in the launch configuration the benchmark times
-(one kivi_encode_* / kivi_decode_* call over every slice of every layer),
-checked on sampled slices against the oracle, plus size-independent
-properties on every element."""
+(one kivi_encode_* / kivi_decode_* call over every slice of every layer).
+The two model-shaped caches are compared with the oracle on every slice,
+bit for bit; the others on sampled slices; size-independent properties are
+checked on every element."""
 
 import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -63,43 +66,82 @@ def _bound_check(kind, cfg, x, xhat, scale, n):
         assert bool(ok.all()), f"error bound violated in slices {s0}..{s0 + 256}"
 
 
-@pytest.mark.parametrize("name", ["llama2_7b_2bit", "mistral_7b_k2v4"])
-def test_full_cache_sampled(name):
-    w = WORKLOADS[name]
-    cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
-    n = w.tokens - w.residual_length
-    S = w.slices
-    _log(f"{name}: generating S={S} T={w.tokens}")
-    k, v = full_cache(w)
-    _log(f"{name}: encode/decode n={n}")
-    kq = U.gpu_encode("k", cfg, k, n)
-    vq = U.gpu_encode("v", cfg, v, n)
-    kd = U.gpu_decode("k", cfg, *kq, n, w.tokens)
-    torch.cuda.synchronize()
-    _log(f"{name}: bound check keys")
-    _bound_check("k", cfg, k, kd, kq[1], n)
-    picks = sample_slices(S, w.number)
-    kh = U.bits16(k[picks]).view(F16)
-    oc, os_, oz = ref.encode_k(kh, n, w.k_bits, w.group_size)
-    U.assert_equal("key codes", U.words(kq[0][picks]), oc.view(np.uint32))
-    U.assert_equal("key scale", U.bits16(kq[1][picks]), os_.view(np.uint16))
-    U.assert_equal("key zero", U.bits16(kq[2][picks]), oz.view(np.uint16))
-    od = ref.decode_k(oc, os_, oz, n, w.k_bits, w.group_size)
-    U.assert_equal("key decode", U.bits16(kd[picks][:, :n]), od.view(np.uint16))
-    assert U.is_poison(U.bits16(kd[picks][:, n:]))
-    del kd
-    vd = U.gpu_decode("v", cfg, *vq, n, w.tokens)
-    torch.cuda.synchronize()
-    _log(f"{name}: bound check values")
-    _bound_check("v", cfg, v, vd, vq[1], n)
-    vh = U.bits16(v[picks]).view(F16)
-    pc, ps, pz = ref.encode_v(vh, n, w.v_bits, w.group_size)
-    U.assert_equal("value codes", U.words(vq[0][picks]), pc.view(np.uint32))
-    U.assert_equal("value scale", U.bits16(vq[1][picks]), ps.view(np.uint16))
-    U.assert_equal("value zero", U.bits16(vq[2][picks]), pz.view(np.uint16))
-    pd = ref.decode_v(pc, ps, pz, n, w.v_bits, w.group_size, w.head_dim)
-    U.assert_equal("value decode", U.bits16(vd[picks][:, :n]), pd.view(np.uint16))
-    _log(f"{name}: sampled slices {picks} bit-exact")
+MODEL_CACHES = ["llama2_7b_2bit", "mistral_7b_k2v4"]
+LAYER_RANGES = [(0, 8), (8, 16), (16, 24), (24, 32)]
+
+
+@pytest.fixture(scope="module")
+def coded():
+    """Lazily built per workload and kept for the module: the whole cache
+    generated on the device and coded in the benchmark's launch configuration
+    (one kivi_encode_k / kivi_encode_v / kivi_decode_k / kivi_decode_v call
+    over every slice of every layer) into poisoned buffers.  Both model
+    caches together hold about 115 GB of device memory."""
+    made = {}
+
+    def get(name):
+        if name not in made:
+            w = WORKLOADS[name]
+            cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
+            n = w.tokens - w.residual_length
+            _log(f"{name}: generating S={w.slices} T={w.tokens}, coding n={n}")
+            k, v = full_cache(w)
+            kq = U.gpu_encode("k", cfg, k, n)
+            vq = U.gpu_encode("v", cfg, v, n)
+            kd = U.gpu_decode("k", cfg, *kq, n, w.tokens)
+            vd = U.gpu_decode("v", cfg, *vq, n, w.tokens)
+            torch.cuda.synchronize()
+            made[name] = dict(w=w, cfg=cfg, n=n, k=k, v=v, kq=kq, vq=vq, kd=kd, vd=vd)
+        return made[name]
+
+    yield get
+    made.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", MODEL_CACHES)
+@pytest.mark.parametrize("layers", LAYER_RANGES, ids=lambda r: f"layers{r[0]}-{r[1] - 1}")
+def test_every_slice_bit_exact(coded, name, layers):
+    """Every slice of the layers in range, keys and values: codes, scale and
+    zero words equal the oracle's encoding, and the decoded tokens its
+    decoding, bit for bit.  Each layer is copied to the host in turn and
+    checked in chunks of slices on a thread pool (the oracle is numpy, whose
+    array loops run without the GIL) while the next layer is copied."""
+    c = coded(name)
+    w, cfg, n = c["w"], c["cfg"], c["n"]
+    spl = w.slices_per_layer
+    chunk = max(1, spl // 16)
+    l0, l1 = layers
+    t0 = time.perf_counter()
+    problems, pending = [], []
+    with ThreadPoolExecutor(U.host_threads()) as pool:
+        for layer in range(l0, l1):
+            s0, s1 = layer * spl, (layer + 1) * spl
+            futs = (U.oracle_check_slices("k", cfg, c["k"], c["kq"], c["kd"], n, s0, s1, pool, chunk)
+                    + U.oracle_check_slices("v", cfg, c["v"], c["vq"], c["vd"], n, s0, s1, pool, chunk))
+            pending.append((layer, futs))
+            while len(pending) > 2:             # at most three layers' host copies alive
+                lay, fs = pending.pop(0)
+                problems += [f"layer {lay}: {m}" for f in fs for m in f.result()]
+        for lay, fs in pending:
+            problems += [f"layer {lay}: {m}" for f in fs for m in f.result()]
+    assert not problems, "\n".join(problems[:20])
+    _log(f"{name}: layers {l0}-{l1 - 1}, slices {l0 * spl}..{l1 * spl - 1}: keys and values bit-exact "
+         f"({time.perf_counter() - t0:.1f} s, {U.host_threads()} threads)")
+
+
+@pytest.mark.parametrize("name", MODEL_CACHES)
+def test_error_bound_and_bounds_every_element(coded, name):
+    """Properties that hold at any size, on every element of the cache:
+    |x - xhat| <= scale/2 + ulp16(x) for normal-scale groups, and the
+    decoders write nothing past the n quantized tokens of a slice."""
+    c = coded(name)
+    cfg, n, w = c["cfg"], c["n"], c["w"]
+    _bound_check("k", cfg, c["k"], c["kd"], c["kq"][1], n)
+    _bound_check("v", cfg, c["v"], c["vd"], c["vq"][1], n)
+    for dec in (c["kd"], c["vd"]):
+        assert bool((dec[:, n:].view(torch.int16) == U.POISON16).all()), "decode wrote past n_tokens"
+    _log(f"{name}: error bound holds on all {2 * w.slices * n * w.head_dim} elements")
 
 
 def test_stream_batch64_full_size_sampled():
@@ -134,8 +176,8 @@ def test_stream_batch64_full_size_sampled():
 
 # ---- next rows at their full sizes ------------------------------------------
 
-@pytest.mark.parametrize("name", ["llama2_7b_2bit", "mistral_7b_k2v4"])
-def test_attention_full_size_sampled(name):
+@pytest.mark.parametrize("name", MODEL_CACHES)
+def test_attention_full_size_sampled(coded, name):
     """Decode attention over the whole cache in one call (the split plan the
     benchmark times).  Sampled slices: the oracle's attention over the
     oracle's own encoding of those slices, within the derived tolerance.
@@ -144,16 +186,11 @@ def test_attention_full_size_sampled(name):
     dequantized values cannot leave it)."""
     from kvsynth import decode_queries
     from oracle import attention_ref as att
-    from tests.test_gpu_attention import _bound
+    from tests.gpu_util import attention_bound as _bound
 
-    w = WORKLOADS[name]
-    cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
+    c = coded(name)
+    w, cfg, k, v, kq, vq = c["w"], c["cfg"], c["k"], c["v"], c["kq"], c["vq"]
     n, R, S, D, G = w.tokens - w.residual_length, w.residual_length, w.slices, w.head_dim, w.group_size
-    _log(f"{name} attention: generating S={S} T={w.tokens}")
-    k, v = full_cache(w)
-    kq, vq = K.alloc_keys(cfg, S, n), K.alloc_values(cfg, S, n)
-    K.kivi_encode_k(cfg, k, n, *kq)
-    K.kivi_encode_v(cfg, v, n, *vq)
     q = decode_queries(w, "cuda")
     out = torch.full_like(q, float("nan"))
     sm_scale = D ** -0.5
