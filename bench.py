@@ -18,6 +18,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -44,19 +45,19 @@ def algorithmic_bytes(kind: str, direction: str, S: int, n: int, D: int, G: int,
 
 def attention_bytes(S: int, n: int, R: int, D: int, G: int, kb: int, vb: int, r: int,
                     n_splits: int) -> dict:
-    """Bytes one decode-attention call must move, per kernel: the packed
-    prefix (codes + sidecars, padding slots of partial key groups included),
-    the fp16 residual, q and the output; with a split plan the partial sums
-    are written by the attention kernel and read back by the merge kernel."""
+    """Bytes of one decode-attention call.  ``method``: what the attention
+    itself must move -- the packed prefix (codes + sidecars, padding slots of
+    partial key groups included), the fp16 residual, q and the output.
+    ``partials``: the split plan's partial sums, written by the attention
+    kernel and read back by the merge kernel (0 with one split), an artefact
+    of this implementation reported on its own."""
     ngk, ngv = -(-n // G), -(-D // G)
     payload = (S * ngk * (G * kb // 32) * D * 4 + 2 * S * ngk * D * 2
                + S * n * ngv * (G * vb // 32) * 4 + 2 * S * n * ngv * 2)
     resid = 2 * S * R * D * 2
     q = out = S * r * D * 2
-    if n_splits > 1:
-        partials = S * n_splits * r * (D + 2) * 4
-        return {"attention": payload + resid + q + partials, "attention_merge": partials + out}
-    return {"attention": payload + resid + q + out}
+    partials = 2 * S * n_splits * r * (D + 2) * 4 if n_splits > 1 else 0
+    return {"method": payload + resid + q + out, "partials": partials}
 
 
 def kernel_source_hash() -> str:
@@ -164,7 +165,7 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str) -> str:
     return "\n".join(lines) + "\n"
 
 
-def attention_bench(w, cfg, k, v, kq, vq, n, args, dev):
+def attention_bench(w, cfg, k, v, kq, vq, n, args, dev, cpu=True):
     """Decode attention of one query token per query head over the cache
     just encoded (quantized prefix + the R fp16 tokens left in k/v), all
     slices in one call; HIP events on the launch stream."""
@@ -205,8 +206,7 @@ def attention_bench(w, cfg, k, v, kq, vq, n, args, dev):
     ms = sorted(runs)[1]
     n_splits = ws_bytes // (S * r * (D + 2) * 4) if ws_bytes else 1
     alg = attention_bytes(S, n, R, D, G, w.k_bits, w.v_bits, r, n_splits)
-    total = sum(alg.values())
-    gbps = total / (ms / 1000.0) / 1e9
+    gbps = alg["method"] / (ms / 1000.0) / 1e9
     res = {
         "what": "softmax attention of one query token per query head over the packed prefix "
                 "plus the fp16 residual, all layers' slices in one call",
@@ -215,13 +215,15 @@ def attention_bench(w, cfg, k, v, kq, vq, n, args, dev):
         "n_splits": n_splits,
         "ms": round(ms, 4),
         "ms_runs": [round(x, 4) for x in runs],
-        "algorithmic_bytes": total,
+        "algorithmic_bytes": alg["method"],
+        "partial_sum_bytes": alg["partials"],
         "achieved_GBps": round(gbps, 1),
         "roofline_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "with_partials_GBps": round((alg["method"] + alg["partials"]) / (ms / 1000.0) / 1e9, 1),
         "fp16_cache_equiv_GBps": round(2 * S * w.tokens * D * 2 / (ms / 1000.0) / 1e9, 1),
         "decode_steps_per_s": round(1000.0 / ms, 1),
     }
-    if not args.no_cpu_baseline:
+    if cpu:
         res["cpu_baseline"] = attention_cpu_baseline(w, k, v, kq, vq, q, n, sm_scale, alg,
                                                      min(args.cpu_budget, 6.0))
     return res
@@ -245,7 +247,7 @@ def attention_cpu_baseline(w, k, v, kq, vq, q, n, sm_scale, alg, budget_s):
         att.decode_attention(qh, kp, vp, n, rk, rv, w.k_bits, w.v_bits, w.group_size, sm_scale)
         spent += time.perf_counter() - t0
         done = sl.stop
-    per_slice = sum(alg.values()) / S
+    per_slice = alg["method"] / S
     return {
         "value": round(per_slice * done / spent / 1e9, 4),
         "unit": "GB/s",
@@ -255,40 +257,52 @@ def attention_cpu_baseline(w, k, v, kq, vq, q, n, sm_scale, alg, budget_s):
     }
 
 
+def _oracle_round_trip(kh, vh, w, cfg, n, kb, vb):
+    """The numpy oracle's encode + decode of one chunk's K and V."""
+    from oracle import fp8_ref as f8
+    from oracle import kivi_ref as ref
+
+    G = cfg.group_size
+    if w.fp8_keys:
+        f8.decode(f8.encode_keys(kh, n))
+    else:
+        kc, ks, kz = ref.encode_k(kh, n, kb, G)
+        ref.decode_k(kc, ks, kz, n, kb, G)
+    vc, vs, vz = ref.encode_v(vh, n, vb, G)
+    ref.decode_v(vc, vs, vz, n, vb, G, cfg.head_dim)
+
+
+def _oracle_chunks(k, v, w, cfg, chunk=8):
+    """Chunks of ``chunk`` slices taken from the layers in turn, with each
+    layer's bits (the oracle's boundary rule for a per-layer mix): yields
+    (slice range, k_bits, v_bits)."""
+    from oracle import layer_mix_ref as mix
+
+    spl = w.slices_per_layer
+    bits = mix.layer_bits(w.layers, w.boundary, (cfg.k_bits, cfg.v_bits), w.boundary_bits)
+    c = 0
+    while True:
+        layer, off = c % w.layers, (c // w.layers) * chunk
+        c += 1
+        if off >= spl:
+            return
+        yield slice(layer * spl + off, layer * spl + min(off + chunk, spl)), bits[layer][0], bits[layer][1]
+
+
 def cpu_baseline(k, v, w, cfg, n, budget_s=12.0):
     """Time the numpy oracle (single thread) on whole slices of the same cache
     until about ``budget_s`` seconds of CPU work; scale to fp16-eq GB/s.
     Chunks of 8 slices are taken from the layers in turn, each coded with
-    its layer's bits (the oracle's boundary rule for a per-layer mix)."""
-    from oracle import fp8_ref as f8
-    from oracle import kivi_ref as ref
-    from oracle import layer_mix_ref as mix
-
-    G = cfg.group_size
-    spl = w.slices_per_layer
-    bits = mix.layer_bits(w.layers, w.boundary, (cfg.k_bits, cfg.v_bits), w.boundary_bits)
-    done = 0
-    spent = 0.0
+    its layer's bits."""
+    done, spent, chunk = 0, 0.0, 8
     S = k.shape[0]
-    chunk = 8
-    c = 0
-    while spent < budget_s and done < S:
-        layer, off = c % w.layers, (c // w.layers) * chunk
-        c += 1
-        if off >= spl:
+    for sl, kb, vb in _oracle_chunks(k, v, w, cfg, chunk):
+        if spent >= budget_s:
             break
-        sl = slice(layer * spl + off, layer * spl + min(off + chunk, spl))
-        kb, vb = bits[layer]
         kh = k[sl].cpu().numpy()
         vh = v[sl].cpu().numpy()
         t0 = time.perf_counter()
-        if w.fp8_keys:
-            f8.decode(f8.encode_keys(kh, n))
-        else:
-            kc, ks, kz = ref.encode_k(kh, n, kb, G)
-            ref.decode_k(kc, ks, kz, n, kb, G)
-        vc, vs, vz = ref.encode_v(vh, n, vb, G)
-        ref.decode_v(vc, vs, vz, n, vb, G, cfg.head_dim)
+        _oracle_round_trip(kh, vh, w, cfg, n, kb, vb)
         spent += time.perf_counter() - t0
         done += sl.stop - sl.start
     fp16_bytes = 2 * 2 * done * n * cfg.head_dim * 2
@@ -301,6 +315,42 @@ def cpu_baseline(k, v, w, cfg, n, budget_s=12.0):
                   f"({done * n} tokens x {cfg.head_dim} channels, K and V), "
                   f"numpy oracle encode+decode, {spent:.1f} s single-threaded "
                   f"(host has {len(os.sched_getaffinity(0))} cores available)",
+    }
+
+
+def cpu_baseline_threads(k, v, w, cfg, n, budget_s=12.0):
+    """The same oracle on the same kind of sample with one thread per
+    available core (numpy runs its array loops without the GIL): batches of
+    chunks are copied to the host, then coded in parallel; only the coding
+    is timed, until about ``budget_s`` seconds of wall-clock."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    threads = len(os.sched_getaffinity(0))
+    chunk = 8
+    S = k.shape[0]
+    chunks = _oracle_chunks(k, v, w, cfg, chunk)
+    done, spent = 0, 0.0
+    with ThreadPoolExecutor(threads) as pool:
+        while spent < budget_s:
+            batch = []
+            for sl, kb, vb in chunks:
+                batch.append((k[sl].cpu().numpy(), v[sl].cpu().numpy(), kb, vb))
+                if len(batch) == 2 * threads:
+                    break
+            if not batch:
+                break
+            t0 = time.perf_counter()
+            list(pool.map(lambda a: _oracle_round_trip(a[0], a[1], w, cfg, n, a[2], a[3]), batch))
+            spent += time.perf_counter() - t0
+            done += sum(a[0].shape[0] for a in batch)
+    fp16_bytes = 2 * 2 * done * n * cfg.head_dim * 2
+    return {
+        "value": round(fp16_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {S} slices in chunks of {chunk} on {threads} threads, numpy oracle "
+                  f"encode+decode, {spent:.1f} s wall-clock",
     }
 
 
@@ -471,52 +521,18 @@ def offload_bench(w, cfg, st, cap, dev):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama2_7b_2bit",
-                    choices=["llama2_7b_2bit", "mistral_7b_k2v4", "single_layer_4bit",
-                             "llama2_7b_k8v4", "llama2_7b_mix", "stream_b64"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--copy-ceiling", action="store_true",
-                    help="also time a plain 4 GiB device-to-device copy (read + write)")
-    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/traffic_<workload>.txt from two rocprofv3 --pmc "
-                         "counter_collection CSVs of this script and exit (no GPU needed)")
-    args = ap.parse_args()
-    if args.summarize_traffic:
-        text = summarize_traffic(args.workload, *args.summarize_traffic)
-        path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.txt")
-        with open(path, "w") as f:
-            f.write(text)
-        print(text, end="")
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this codec benchmark runs on one GPU only; "
-                                   "--gpus must be 1 (slices shard across GPUs with no exchange, "
-                                   "so per-GPU throughput is the figure)"}), flush=True)
-        sys.exit(2)
+def _median(xs):
+    return float(statistics.median(xs))
 
+
+def build_cache(w, dev):
+    """The workload's K and V of all layers, [L*B*H, T, D] fp16 each, generated
+    on the device one layer at a time."""
     import torch
 
-    import kv_cache_quantization_codec_amd as K
-    from kvsynth import WORKLOADS, layer_kv
+    from kvsynth import layer_kv
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    K.binding.lib()
-    w = WORKLOADS[args.workload]
-    if w.steps:
-        print(json.dumps(stream_bench(w, args)), flush=True)
-        return
-    cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
-    S, T, D, G = w.slices, w.tokens, w.head_dim, w.group_size
-    n = T - w.residual_length
-    dev = torch.device("cuda:0")
-
-    k = torch.empty((S, T, D), dtype=torch.float16, device=dev)
+    k = torch.empty((w.slices, w.tokens, w.head_dim), dtype=torch.float16, device=dev)
     v = torch.empty_like(k)
     spl = w.slices_per_layer
     for layer in range(w.layers):
@@ -524,10 +540,58 @@ def main():
         k[layer * spl:(layer + 1) * spl] = kl
         v[layer * spl:(layer + 1) * spl] = vl
         del kl, vl
+    return k, v
+
+
+def time_steps(calls, steps, warmup):
+    """Runs ``warmup`` untimed steps, then ``steps`` timed steps of the calls
+    in order, with a HIP event (on torch's current stream, where the binding
+    launches) before and after every call.  Returns (wall ms per step,
+    per-call ms lists, per-step ms list)."""
+    import torch
+
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        for j, c in enumerate(calls):
+            c()
+            ev[i][j + 1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per_call = [[ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)] for j in range(len(calls))]
+    per_step = [ev[i][0].elapsed_time(ev[i][len(calls)]) for i in range(steps)]
+    return (t1 - t0) * 1000.0 / steps, per_call, per_step
+
+
+def codec_bench(w, args, dev, *, attention: bool, cpu: bool, per_layer: bool = False,
+                steps: int | None = None):
+    """One workload's full-cache step (encode K, encode V, decode K, decode V
+    over every slice), its roofline figures, and optionally decode attention
+    over the same cache, the oracle timed beside it, and the same step as a
+    loop of one call per layer.  Returns the result dict; the device tensors
+    are released on return."""
+    import torch
+
+    import kv_cache_quantization_codec_amd as K
+
+    steps = args.steps if steps is None else steps
+    cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
+    S, T, D, G = w.slices, w.tokens, w.head_dim, w.group_size
+    n = T - w.residual_length
+    k, v = build_cache(w, dev)
     ko = torch.empty((S, n, D), dtype=torch.float16, device=dev)
     vo = torch.empty_like(ko)
     names = ["encode_k", "encode_v", "decode_k", "decode_v"]
     launches = {nm: 1 for nm in names}
+    spl = w.slices_per_layer
+    kq = vq = None
     if w.boundary:
         # per-layer bit mix: the library's boundary rule, one config per layer,
         # each run of equal layers in one allocation (one launch per run)
@@ -565,25 +629,9 @@ def main():
             lambda: K.kivi_decode_k(cfg, *kq, n, ko),
             lambda: K.kivi_decode_v(cfg, *vq, n, vo),
         ]
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        for c in calls:
-            c()
-    torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record()
-        for j, c in enumerate(calls):
-            c()
-            ev[i][j + 1].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1000.0 / args.steps
-    per_kernel_ms = {nm: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / args.steps
-                     for j, nm in enumerate(names)}
+    ms_step, per_call, per_step = time_steps(calls, steps, args.warmup)
+    per_kernel_ms = {nm: sum(per_call[j]) / steps for j, nm in enumerate(names)}
+    per_kernel_med = {nm: _median(per_call[j]) for j, nm in enumerate(names)}
 
     fp16_eq = 2 * 2 * S * n * D * 2                  # K and V, encode + decode
     bits = {"encode_k": w.k_bits, "decode_k": w.k_bits, "encode_v": w.v_bits, "decode_v": w.v_bits}
@@ -597,15 +645,16 @@ def main():
     moved = sum(alg.values())
     dom = max(names, key=lambda nm: per_kernel_ms[nm])
     achieved = alg[dom] / (per_kernel_ms[dom] / 1000.0) / 1e9
-    traffic = measured_traffic(dom, args.workload)
+    traffic = measured_traffic(dom, w_key(w))
     tokens = w.batch * n                              # sequence positions, all layers and heads
+    med_step = _median(per_step)
 
     out = {
         "metric": "KV encode+decode GB/s (fp16-equivalent) and % of HBM roofline, 1 MI355X",
         "value": round(fp16_eq / (ms_step / 1000.0) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
@@ -621,10 +670,13 @@ def main():
             "key_format": "fp8_e4m3" if w.fp8_keys else "kivi",
             **({"boundary_layers": sorted(prot), "boundary_bits": list(w.boundary_bits)} if w.boundary else {}),
         },
+        "ms_per_step_median": round(med_step, 4),
         "moved_GBps": round(moved / (ms_step / 1000.0) / 1e9, 2),
         "hbm_roofline_frac_step": round(moved / (ms_step / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
+        "hbm_roofline_frac_step_median": round(moved / (med_step / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(tokens / (ms_step / 1000.0), 1),
         "kernel_ms": {nm: round(x, 4) for nm, x in per_kernel_ms.items()},
+        "kernel_ms_median": {nm: round(x, 4) for nm, x in per_kernel_med.items()},
         "kernel_GBps": {nm: round(alg[nm] / (per_kernel_ms[nm] / 1000.0) / 1e9, 1) for nm in names},
         "roofline": {
             "bound": "hbm",
@@ -638,12 +690,170 @@ def main():
             **({"launches_per_call": launches[dom]} if launches[dom] > 1 else {}),
         },
     }
-    if not w.fp8_keys and not w.boundary:
-        out["attention"] = attention_bench(w, cfg, k, v, kq, vq, n, args, dev)
-    if args.copy_ceiling:
-        out["copy_ceiling_GBps"] = copy_ceiling(dev)
-    if not args.no_cpu_baseline:
+    if per_layer and not w.fp8_keys and not w.boundary:
+        out["per_layer_loop"] = per_layer_bench(w, cfg, k, v, kq, vq, ko, vo, n, alg, steps, args.warmup)
+    if attention and not w.fp8_keys and not w.boundary:
+        out["attention"] = attention_bench(w, cfg, k, v, kq, vq, n, args, dev, cpu)
+    if cpu:
         out["cpu_baseline"] = cpu_baseline(k, v, w, cfg, n, args.cpu_budget)
+        out["cpu_baseline_all_cores"] = cpu_baseline_threads(k, v, w, cfg, n, args.cpu_budget)
+    del k, v, ko, vo, kq, vq, calls
+    torch.cuda.empty_cache()
+    return out
+
+
+def w_key(w):
+    """The WORKLOADS key of a workload."""
+    from kvsynth import WORKLOADS
+    return next(key for key, x in WORKLOADS.items() if x is w)
+
+
+def per_layer_bench(w, cfg, k, v, kq, vq, ko, vo, n, alg, steps, warmup):
+    """The same step as a loop over layers: each kernel called once per layer
+    (slices_per_layer slices a call), the way a model's cache is coded layer
+    by layer; HIP events around each kernel's run of calls."""
+    import kv_cache_quantization_codec_amd as K
+
+    spl = w.slices_per_layer
+    L = w.layers
+    lay = [slice(l * spl, (l + 1) * spl) for l in range(L)]
+    kql = [tuple(t[sl] for t in kq) for sl in lay]
+    vql = [tuple(t[sl] for t in vq) for sl in lay]
+    kl, vl, kol, vol = ([x[sl] for sl in lay] for x in (k, v, ko, vo))
+    calls = [
+        lambda: [K.kivi_encode_k(cfg, kl[l], n, *kql[l]) for l in range(L)],
+        lambda: [K.kivi_encode_v(cfg, vl[l], n, *vql[l]) for l in range(L)],
+        lambda: [K.kivi_decode_k(cfg, *kql[l], n, kol[l]) for l in range(L)],
+        lambda: [K.kivi_decode_v(cfg, *vql[l], n, vol[l]) for l in range(L)],
+    ]
+    names = ["encode_k", "encode_v", "decode_k", "decode_v"]
+    ms_step, per_call, per_step = time_steps(calls, steps, warmup)
+    med = _median(per_step)
+    moved = sum(alg.values())
+    kms = {nm: _median(per_call[j]) for j, nm in enumerate(names)}
+    slow = max(kms, key=kms.get)
+    return {
+        "what": f"the same step as {L} calls per kernel, one per layer of {spl} slices",
+        "calls_per_kernel": L,
+        "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(med, 4),
+        "kernel_ms_median": {nm: round(x, 4) for nm, x in kms.items()},
+        "moved_GBps": round(moved / (med / 1000.0) / 1e9, 2),
+        "hbm_roofline_frac_step": round(moved / (med / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
+        "slowest_kernel": slow,
+        "slowest_kernel_frac": round(alg[slow] / (kms[slow] / 1000.0) / 1e9 / HBM_PEAK_GBPS, 4),
+    }
+
+
+def workload_summary(res: dict) -> dict:
+    """The figures of a secondary workload's bench result kept on the main line."""
+    keep = ("config", "ms_per_step", "ms_per_step_median", "value", "moved_GBps", "hbm_roofline_frac_step",
+            "hbm_roofline_frac_step_median", "tokens_per_s", "kernel_ms_median", "kernel_GBps")
+    out = {k: res[k] for k in keep if k in res}
+    out["value_unit"] = "GB/s fp16-equivalent"
+    out["slowest_kernel"] = res["roofline"]["kernel"]
+    out["slowest_kernel_frac"] = res["roofline"]["frac"]
+    if "attention" in res:
+        a = res["attention"]
+        out["attention"] = {k: a[k] for k in ("q_per_kv", "n_splits", "ms", "ms_runs", "algorithmic_bytes",
+                                              "partial_sum_bytes", "achieved_GBps", "roofline_frac",
+                                              "fp16_cache_equiv_GBps") if k in a}
+    return out
+
+
+def latency_bench(w, args, dev, reps=200):
+    """A cache too small to stream (the single-layer workload): the step's
+    latency in microseconds, median over ``reps`` steps."""
+    import kv_cache_quantization_codec_amd as K
+
+    cfg = K.Config(w.k_bits, w.v_bits, w.group_size, w.residual_length, w.head_dim)
+    S, D = w.slices, w.head_dim
+    n = w.tokens - w.residual_length
+    k, v = build_cache(w, dev)
+    kq, vq = K.alloc_keys(cfg, S, n, dev), K.alloc_values(cfg, S, n, dev)
+    ko, vo = k.new_empty((S, n, D)), v.new_empty((S, n, D))
+    calls = [lambda: K.kivi_encode_k(cfg, k, n, *kq), lambda: K.kivi_encode_v(cfg, v, n, *vq),
+             lambda: K.kivi_decode_k(cfg, *kq, n, ko), lambda: K.kivi_decode_v(cfg, *vq, n, vo)]
+    _, per_call, per_step = time_steps(calls, reps, 20)
+    names = ["encode_k", "encode_v", "decode_k", "decode_v"]
+    moved = sum(algorithmic_bytes(nm[-1], nm[:6], S, n, D, w.group_size, w.k_bits if nm[-1] == "k"
+                                  else w.v_bits) for nm in names)
+    return {
+        "config": {"workload": w.name, "slices": S, "seq_len": w.tokens, "quantized_tokens": n,
+                   "k_bits": w.k_bits, "v_bits": w.v_bits, "group_size": w.group_size},
+        "us_per_step_median": round(_median(per_step) * 1000.0, 2),
+        "kernel_us_median": {nm: round(_median(per_call[j]) * 1000.0, 2) for j, nm in enumerate(names)},
+        "moved_bytes": moved,
+        "steps": reps,
+        "note": "latency bound: 4 MB moved per step, below a kernel launch's cost",
+    }
+
+
+def stream_summary(res: dict) -> dict:
+    keep = ("config", "value", "unit", "p99_us", "flush_steps", "flush_p50_us", "flush_p99_us",
+            "append_p50_us", "append_p99_us", "append_GBps", "flush_GBps", "prefill_ms", "prefill_GBps",
+            "final_state", "offload_restore")
+    out = {k: res[k] for k in keep if k in res}
+    out["value_is"] = "p50 step latency over all steps"
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2_7b_2bit",
+                    choices=["llama2_7b_2bit", "mistral_7b_k2v4", "single_layer_4bit",
+                             "llama2_7b_k8v4", "llama2_7b_mix", "stream_b64"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the chosen workload (no per-layer loop, secondary workloads "
+                         "or copy ceiling): for profiler runs")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="also time a plain 4 GiB device-to-device copy (always done in the default run)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.txt from two rocprofv3 --pmc "
+                         "counter_collection CSVs of this script and exit (no GPU needed)")
+    args = ap.parse_args()
+    if args.summarize_traffic:
+        text = summarize_traffic(args.workload, *args.summarize_traffic)
+        path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.txt")
+        with open(path, "w") as f:
+            f.write(text)
+        print(text, end="")
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this codec benchmark runs on one GPU only; "
+                                   "--gpus must be 1 (slices shard across GPUs with no exchange, "
+                                   "so per-GPU throughput is the figure)"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_quantization_codec_amd as K
+    from kvsynth import WORKLOADS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K.binding.lib()
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    if w.steps:
+        print(json.dumps(stream_bench(w, args)), flush=True)
+        return
+    full = args.workload == "llama2_7b_2bit" and not args.headline_only
+    cpu = not args.no_cpu_baseline
+    out = codec_bench(w, args, dev, attention=True, cpu=cpu, per_layer=full)
+    if full:
+        # the other workloads of the same measurement, each after the previous
+        # one's device memory is released
+        out["mistral_7b_k2v4"] = workload_summary(
+            codec_bench(WORKLOADS["mistral_7b_k2v4"], args, dev, attention=True, cpu=False))
+        out["single_layer_4bit"] = latency_bench(WORKLOADS["single_layer_4bit"], args, dev)
+        out["stream_b64"] = stream_summary(stream_bench(WORKLOADS["stream_b64"], args))
+    if full or args.copy_ceiling:
+        out["copy_ceiling_GBps"] = copy_ceiling(dev)
     print(json.dumps(out), flush=True)
 
 

@@ -59,19 +59,31 @@ def test_partial_groups_count_their_padding():
 
 
 def test_attention_bytes_llama_shape():
-    # packed prefix, fp16 residual, q, partial sums (5 splits, 1 head,
-    # 128 + 2 floats each) written by the attention kernel and read by the
-    # merge kernel, which writes the output
+    # what attention must move: the packed prefix, the fp16 residual, q and
+    # the output; the partial sums of a split plan (5 splits, 1 head, 128 + 2
+    # floats each, written by the attention kernel and read back by the
+    # merge kernel) are counted on their own
     payload = 1_040_187_392 + 520_093_696 + 1_040_187_392 + 520_093_696
     resid = 2 * 8192 * 128 * 128 * 2
     q = out = 8192 * 128 * 2
     partials = 8192 * 5 * 130 * 4
     got = bench.attention_bytes(8192, 3968, 128, 128, 32, 2, 2, 1, 5)
-    assert got == {"attention": payload + resid + q + partials, "attention_merge": partials + out}
-    assert sum(got.values()) == 3_704_225_792
-    # one split: no partial sums, the attention kernel writes the output
+    assert got == {"method": payload + resid + q + out, "partials": 2 * partials}
+    assert got["method"] == 3_661_627_392
+    assert got["method"] + got["partials"] == 3_704_225_792
+    # one split: no partial sums
     one = bench.attention_bytes(8192, 3968, 128, 128, 32, 2, 2, 1, 1)
-    assert one == {"attention": payload + resid + q + out}
+    assert one == {"method": payload + resid + q + out, "partials": 0}
+
+
+def test_attention_bytes_mistral_shape():
+    # 4096 slices x 16256 quantized tokens, keys 2-bit and values 4-bit,
+    # 4 query heads per KV slice, 128 fp16 residual tokens
+    payload = (4096 * 508 * 2 * 128 * 4 + 2 * 4096 * 508 * 128 * 2
+               + 4096 * 16256 * 16 * 4 + 2 * 4096 * 16256 * 4 * 2)
+    got = bench.attention_bytes(4096, 16256, 128, 128, 32, 2, 4, 4, 9)
+    assert got["method"] == payload + 2 * 4096 * 128 * 128 * 2 + 2 * 4096 * 4 * 128 * 2
+    assert got["partials"] == 2 * 4096 * 9 * 4 * 130 * 4
 
 
 def test_more_than_one_gpu_is_refused():
