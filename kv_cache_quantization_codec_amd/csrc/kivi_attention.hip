@@ -29,8 +29,17 @@
 //   key zero-point term (identical in every token column of a group) is an
 //   MFMA of q against the group's zeros when a KV slice serves 3-8 query
 //   heads, and an fp32 dot product reduced over the wave for 1-2.
+// * Value codes are loaded so that the lanes of one load instruction read
+//   whole consecutive token rows (a code unit is one word column of tokens
+//   p, p + 16, p + 8, p + 24); the value product's token order follows the
+//   units (vslot), and the weight operands are written in that order.
 // * Three kernel variants by the bound on query heads per KV slice (2, 4,
-//   8) size the LDS operand rows.
+//   8) size the LDS operand rows.  Lane rows of the value-weight step that
+//   hold no head take a share of the value groups.  The variants for 3-8
+//   heads run a slice's full 32-token blocks without per-token bounds; the
+//   1-2 head variant keeps one loop (its registers and code size decide).
+// * The logit scale is folded into the pre-scaled query (1-2 heads) or the
+//   column factor and key zero term (3-8 heads).
 // * Online softmax in base 2 per 32-token block; heads live in MFMA rows, so
 //   each lane holds two heads' scores of one token and the row reductions
 //   are DPP moves inside a 16-lane row.
@@ -44,6 +53,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "../../include/kivi.h"
 #include "kivi_launch.h"
@@ -156,6 +166,11 @@ __device__ __forceinline__ h8 codes8(uint32_t d0, uint32_t d1, uint32_t mask) {
 // only stops the compiler from moving LDS accesses across the point.
 __device__ __forceinline__ void lds_order() { __asm__ __volatile__("" ::: "memory"); }
 
+// Operand slot of value-product token t in [0, 16) (token t + 16 takes the
+// next slot): a lane's eight slots 8kq .. 8kq + 7 hold the tokens of code
+// units p = 2kq and 2kq + 1, each unit being tokens p, p + 16, p + 8, p + 24.
+__device__ __forceinline__ int vslot(int t) { return 8 * ((t & 7) >> 1) + 4 * (t & 1) + 2 * (t >> 3); }
+
 // 16-byte LDS read as an MFMA operand.
 __device__ __forceinline__ h8 lds_h8(const void* p) {
     return __builtin_bit_cast(h8, *reinterpret_cast<const u32x4*>(p));
@@ -200,8 +215,8 @@ struct alignas(16) Smem {
     f16 aq[operand_rows<RMAX>()][D + 8];   // q*s of the current key group, hi/lo rows
     f16 kz[D];                             // zeros of the current key group
     uint32_t kt[KB][D];                    // key codes of a 32-token block: [word row][channel/4][byte]
-    uint32_t vt[VB * D / 32][32];          // value codes: [word column][token unit][byte]
-    f16 vz[4][kTokStride];                 // value zeros, [group][operand slot of the row]
+    uint32_t vt[VB * D / 32][32 + 4];      // value codes: [word column][token unit][byte] (padded)
+    f16 vz[5][kTokStride];                 // value zeros, [group][operand slot of the row]; row 4 zero
     float vs[4][32 + 4];                   // value scales, [group][row]
     f16 ap[4][operand_rows<RMAX>()][kTokStride];   // p*s per value group, hi/lo rows
     f16 apz[operand_rows<RMAX>()][kTokStride];     // p, hi/lo rows
@@ -332,6 +347,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     for (int i = L; i < OROWS * (D + 8); i += kWave) (&sm.aq[0][0])[i] = (f16)0;
     for (int i = L; i < 4 * OROWS * kTokStride; i += kWave) (&sm.ap[0][0][0])[i] = (f16)0;
     for (int i = L; i < OROWS * kTokStride; i += kWave) (&sm.apz[0][0])[i] = (f16)0;
+    if (L < kTokStride) sm.vz[4][L] = (f16)0;
     // the queries to LDS; rows of heads >= r and the zero row are zero
     for (int i = L; i < (RMAX + 1) * D / 8; i += kWave) {
         const int h = i / (D / 8), c = 8 * (i - h * (D / 8));
@@ -445,8 +461,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         for (int h = 0; h < 2; ++h)
             if (h < r && pair_live) {
                 const uint32_t qw = *reinterpret_cast<const uint32_t*>(a.q + (s * r + h) * D + 2 * L);
-                qreg[h][0] = lo_f(qw);
-                qreg[h][1] = hi_f(qw);
+                qreg[h][0] = lo_f(qw) * a.logit_scale;
+                qreg[h][1] = hi_f(qw) * a.logit_scale;
             }
     }
 
@@ -464,9 +480,11 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     };
     // Addresses: wave-uniform bases of the block (64-bit, scalar) plus lane
     // byte offsets below 2^32 (at most 32 rows of one block).
-    auto load = [&](int blk, Stage& st) {
+    auto load = [&](int blk, Stage& st, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;  // all 32 rows of the block are valid
         const int t0 = 32 * blk, g = t0 / G;
         const int last = n - 1 - t0;                      // rows past n read row n-1 (weights 0)
+        auto clamp = [&](int row) { return FULL ? row : min(row, last); };
         const uint32_t* srck = kcs + ((int64_t)g * Wk + ((t0 % G) / 32) * KB) * D;
         const uint32_t* vrow = vcs + (int64_t)t0 * WPT;
         const uint16_t* srow = vss + (int64_t)t0 * NGV;
@@ -481,12 +499,13 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         for (int i = 0; i < VV; ++i) {
             const int u = L + kWave * i;
             if (VU % kWave == 0 || u < VU) {
-                // word column c2, tokens 2p, 16 + 2p, 2p + 1, 17 + 2p (the
-                // value product's token order, see below)
-                const int c2 = u >> 3, p = u & 7;
+                // word column c2, tokens p, p + 16, p + 8, p + 24 (the value
+                // product's token order, see below); the lanes of one load
+                // instruction cover whole consecutive token rows
+                const int c2 = u % RW, p = u / RW;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int row = min(2 * p + (e >> 1) + 16 * (e & 1), last);
+                    const int row = clamp(p + 16 * (e & 1) + 8 * (e >> 1));
                     st.v[i][e] = __builtin_nontemporal_load(at_byte(vrow, 4u * (uint32_t)(row * WPT + c2)));
                 }
             }
@@ -496,7 +515,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             const int e = L + kWave * i;
             if (32 * NGV % kWave == 0 || e < 32 * NGV) {
                 const int row = e / NGV, gv = e - row * NGV;
-                const uint32_t off = 2u * (uint32_t)(min(row, last) * NGV + gv);   // masked below
+                const uint32_t off = 2u * (uint32_t)(clamp(row) * NGV + gv);   // masked below
                 st.vsb[i] = *at_byte(srow, off);
                 st.vzb[i] = *at_byte(zrow, off);
             }
@@ -506,7 +525,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             st.kz = *at_byte(reinterpret_cast<const uint32_t*>(kzs + (int64_t)g * D), 4u * L);
         }
     };
-    auto commit = [&](int blk, const Stage& st) {
+    auto commit = [&](int blk, const Stage& st, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         const int t0 = 32 * blk;
 #pragma unroll
         for (int i = 0; i < KV; ++i) {
@@ -522,7 +542,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             const int u = L + kWave * i;
             if (VU % kWave == 0 || u < VU) {
                 const uint32_t* w = st.v[i];
-                *reinterpret_cast<u32x4*>(&sm.vt[0][0] + 4 * u) = bytes_t4(w[0], w[1], w[2], w[3]);
+                *reinterpret_cast<u32x4*>(&sm.vt[u % RW][4 * (u / RW)]) = bytes_t4(w[0], w[1], w[2], w[3]);
             }
         }
 #pragma unroll
@@ -530,9 +550,9 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             const int e = L + kWave * i;
             if (32 * NGV % kWave == 0 || e < 32 * NGV) {
                 const int row = e / NGV, gv = e - row * NGV;
-                const bool live = t0 + row < n;
+                const bool live = FULL || t0 + row < n;
                 sm.vs[gv][row] = live ? (float)__builtin_bit_cast(f16, st.vsb[i]) : 0.0f;
-                sm.vz[gv][2 * (row & 15) + (row >> 4)] = __builtin_bit_cast(f16, live ? st.vzb[i] : (uint16_t)0);
+                sm.vz[gv][vslot(row & 15) + (row >> 4)] = __builtin_bit_cast(f16, live ? st.vzb[i] : (uint16_t)0);
             }
         }
         // a new key group: q*s operand rows (fp32 product split hi/lo) and zeros
@@ -567,17 +587,27 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         }
     };
 
+    const int js = vslot(j);                              // operand slots of tokens j, j + 16
     const CodePos<KB> kpos(j % (32 / KB));
     const CodePos<VB> vpos(j % (32 / VB));
+    // the logit scale rides on the column factor where q is not pre-scaled
+    const float kcol = RMAX == 2 ? kpos.col : kpos.col * a.logit_scale;
+    const int zrow = j < ngv ? j : 4;                     // value-zero operand row (4: zeros)
     f4 zk = f4{0, 0, 0, 0};
     Stage stage;
-    if (b0 < b1) load(b0, stage);
+    // blocks [b0, bf) hold 32 valid tokens each; only the slice's last block
+    // may be partial and needs the per-token bounds
+    const int bf = RMAX == 2 ? b0 : min(b1, n / 32);
+    if (b0 < bf) load(b0, stage, std::true_type{});
+    else if (b0 < b1) load(b0, stage, std::false_type{});
 
-    for (int blk = b0; blk < b1; ++blk) {
+    auto block = [&](int blk, auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
         const int t0 = 32 * blk;
-        commit(blk, stage);
+        commit(blk, stage, full_tag);
         lds_order();
-        if (blk + 1 < b1) load(blk + 1, stage);
+        if (blk + 1 < bf) load(blk + 1, stage, std::true_type{});
+        else if (blk + 1 < b1) load(blk + 1, stage, std::false_type{});
 
         // keys: the zero-point term of a new group, then the scores of two
         // 16-token tiles
@@ -599,34 +629,102 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             }
         }
         float xa[2], xb[2];
-        const float za = RMAX == 2 ? zg0 : zk[0], zb = RMAX == 2 ? zg1 : zk[2];
+        const float za = RMAX == 2 ? zg0 : zk[0] * a.logit_scale, zb = RMAX == 2 ? zg1 : zk[2] * a.logit_scale;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const bool valid = t0 + 16 * tt + j < n;
-            xa[tt] = valid ? ((sc[tt][0] + sc[tt][1]) * kpos.col + za) * a.logit_scale : kNegInf;
-            xb[tt] = valid ? ((sc[tt][2] + sc[tt][3]) * kpos.col + zb) * a.logit_scale : kNegInf;
+            const bool valid = FULL || t0 + 16 * tt + j < n;
+            xa[tt] = valid ? (sc[tt][0] + sc[tt][1]) * kcol + za : kNegInf;
+            xb[tt] = valid ? (sc[tt][2] + sc[tt][3]) * kcol + zb : kNegInf;
         }
         softmax_block(acc, xa, xb);
 
-        // values: the product runs over the block's tokens in the order
-        // 0, 16, 1, 17, ..., 15, 31 (operand slot 2m is token m, slot 2m + 1
-        // token 16 + m), so the two weights a lane holds (tokens j and
-        // 16 + j of heads 2kq and 2kq+1) fill one dword of each hi/lo
-        // operand row: p itself, and p*s for every value group
+        // values: the product runs over the block's tokens in the slot
+        // order of vslot (tokens t and t + 16 in adjacent slots), so the two
+        // weights a lane holds (tokens j and 16 + j of heads 2kq and 2kq+1)
+        // fill one dword of each hi/lo operand row: p itself, and p*s for
+        // every value group.  Lane rows that hold no head take a share of
+        // the groups, with the weights copied from the lanes that hold them.
+        if constexpr (RMAX == 4 && NGV >= 2) {
+            // heads live in lane rows kq = 0, 1; rows 2, 3 take the upper half
+            // of the value groups of the heads of row kq - 2 (their weights
+            // copied from lane L ^ 32)
+            float ya[2], yb[2];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int h = 2 * kq + hh;
-            if (h < r) {
-                const float p0 = hh ? xb[0] : xa[0], p1 = hh ? xb[1] : xa[1];
-                uint32_t hi, lo;
-                split_prod2(p0, 1.0f, p1, 1.0f, hi, lo);
-                *reinterpret_cast<uint32_t*>(&sm.apz[2 * h][2 * j]) = hi;
-                *reinterpret_cast<uint32_t*>(&sm.apz[2 * h + 1][2 * j]) = lo;
+            for (int tt = 0; tt < 2; ++tt) {
+                ya[tt] = __shfl_xor(xa[tt], 32, kWave);
+                yb[tt] = __shfl_xor(xb[tt], 32, kWave);
+            }
+            const bool upper = kq >= 2;
+            constexpr int HG = NGV / 2;                    // groups of the lower rows
 #pragma unroll
-                for (int gv = 0; gv < NGV; ++gv) {
-                    split_prod2(p0, sm.vs[gv][j], p1, sm.vs[gv][16 + j], hi, lo);
-                    *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h][2 * j]) = hi;
-                    *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h + 1][2 * j]) = lo;
+            for (int hh = 0; hh < 2; ++hh) {
+                const int h = 2 * (kq & 1) + hh;
+                if (h < r) {
+                    const float p0 = upper ? (hh ? yb[0] : ya[0]) : (hh ? xb[0] : xa[0]);
+                    const float p1 = upper ? (hh ? yb[1] : ya[1]) : (hh ? xb[1] : xa[1]);
+                    uint32_t hi, lo;
+                    if (!upper) {
+                        split_prod2(p0, 1.0f, p1, 1.0f, hi, lo);
+                        *reinterpret_cast<uint32_t*>(&sm.apz[2 * h][js]) = hi;
+                        *reinterpret_cast<uint32_t*>(&sm.apz[2 * h + 1][js]) = lo;
+                    }
+#pragma unroll
+                    for (int g2 = 0; g2 < NGV - HG; ++g2) {
+                        const int gv = upper ? HG + g2 : g2;
+                        if (upper || g2 < HG) {
+                            split_prod2(p0, sm.vs[gv][j], p1, sm.vs[gv][16 + j], hi, lo);
+                            *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h][js]) = hi;
+                            *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h + 1][js]) = lo;
+                        }
+                    }
+                }
+            }
+        } else if constexpr (RMAX == 2 && NGV >= 2) {
+            // the heads live in lane row kq = 0; row kq takes value groups
+            // kq, kq + 4, ... of both heads (weights copied from lane j)
+            float ya[2], yb[2];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                ya[tt] = __shfl(xa[tt], j, kWave);
+                yb[tt] = r > 1 ? __shfl(xb[tt], j, kWave) : 0.0f;
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                if (hh < r) {
+                    const float p0 = hh ? yb[0] : ya[0], p1 = hh ? yb[1] : ya[1];
+                    uint32_t hi, lo;
+                    if (kq == 0) {
+                        split_prod2(p0, 1.0f, p1, 1.0f, hi, lo);
+                        *reinterpret_cast<uint32_t*>(&sm.apz[2 * hh][js]) = hi;
+                        *reinterpret_cast<uint32_t*>(&sm.apz[2 * hh + 1][js]) = lo;
+                    }
+#pragma unroll
+                    for (int g4 = 0; g4 < (NGV + 3) / 4; ++g4) {
+                        const int gv = 4 * g4 + kq;
+                        if (gv < NGV) {
+                            split_prod2(p0, sm.vs[gv][j], p1, sm.vs[gv][16 + j], hi, lo);
+                            *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * hh][js]) = hi;
+                            *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * hh + 1][js]) = lo;
+                        }
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int h = 2 * kq + hh;
+                if (h < r) {
+                    const float p0 = hh ? xb[0] : xa[0], p1 = hh ? xb[1] : xa[1];
+                    uint32_t hi, lo;
+                    split_prod2(p0, 1.0f, p1, 1.0f, hi, lo);
+                    *reinterpret_cast<uint32_t*>(&sm.apz[2 * h][js]) = hi;
+                    *reinterpret_cast<uint32_t*>(&sm.apz[2 * h + 1][js]) = lo;
+    #pragma unroll
+                    for (int gv = 0; gv < NGV; ++gv) {
+                        split_prod2(p0, sm.vs[gv][j], p1, sm.vs[gv][16 + j], hi, lo);
+                        *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h][js]) = hi;
+                        *reinterpret_cast<uint32_t*>(&sm.ap[gv][2 * h + 1][js]) = lo;
+                    }
                 }
             }
         }
@@ -634,8 +732,8 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         // values: zero-point term over all groups at once (columns = groups)
         {
             const h8 pz = lds_h8(&sm.apz[jr][8 * kq]);
-            const h8 bz = lds_h8(&sm.vz[j < ngv ? j : 0][8 * kq]);
-            acc.z = mfma(pz, j < ngv ? bz : __builtin_bit_cast(h8, u32x4{0, 0, 0, 0}), acc.z);
+            const h8 bz = lds_h8(&sm.vz[zrow][8 * kq]);
+            acc.z = mfma(pz, bz, acc.z);
         }
 #pragma unroll
         for (int nt = 0; nt < NT16; ++nt) {
@@ -647,7 +745,10 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             acc.o[nt] = mfma(aop, bop, acc.o[nt]);
         }
         lds_order();   // the next block's commit overwrites what this one read
-    }
+    };
+    int blk = b0;
+    for (; blk < bf; ++blk) block(blk, std::true_type{});
+    for (; blk < b1; ++blk) block(blk, std::false_type{});
 
     // output = code term * column factor + zero term of the channel's group;
     // the zero term of group gv sits in column gv of the same 16-lane row
