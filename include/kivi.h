@@ -115,7 +115,8 @@ int kivi_validate_config(const kivi_config* cfg);
 
 /* Sizes per slice, for a capacity of n_tokens quantized tokens (CacheSeek
  * PR #4: the manager accounts the stored payload size itself).  Return -1
- * for an invalid configuration or n_tokens < 0.
+ * for an invalid configuration, n_tokens < 0 or n_tokens above 2^30 (the
+ * per-slice token limit of every call).
  *   kivi_k_code_words  int32 words of key codes     = NG_k(n)*W_k*D
  *   kivi_k_stat_elems  fp16 elements of ONE key sidecar (scale or zero)
  *                                                   = NG_k(n)*D

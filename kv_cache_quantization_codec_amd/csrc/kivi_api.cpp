@@ -67,7 +67,7 @@ int check_common(const kivi_config* c, int64_t n_slices, int64_t n_tokens, int64
     int64_t need = 0;
     if (!mul_ok(n_tokens, c->head_dim, &need) || fp16_stride < need) return KIVI_E_SHAPE;
     int64_t total = 0;
-    if (!mul_ok(n_slices, fp16_stride, &total)) return KIVI_E_SHAPE;
+    if (!mul_ok(n_slices, fp16_stride, &total) || !mul_ok(total, 2, &total)) return KIVI_E_SHAPE;
     const int64_t words = keys ? k_words(c, cap_tokens) : v_words(c, cap_tokens);
     if (!mul_ok(n_slices, words, &total) || !mul_ok(total, 4, &total)) return KIVI_E_SHAPE;
     return KIVI_OK;
@@ -415,16 +415,16 @@ int kivi_last_hip_error(void) { return g_last_hip_error; }
 int kivi_validate_config(const kivi_config* cfg) { return check_config(cfg); }
 
 int64_t kivi_k_code_words(const kivi_config* cfg, int64_t n) {
-    return (check_config(cfg) || n < 0) ? -1 : k_words(cfg, n);
+    return (check_config(cfg) || n < 0 || n > kMaxTokens) ? -1 : k_words(cfg, n);
 }
 int64_t kivi_k_stat_elems(const kivi_config* cfg, int64_t n) {
-    return (check_config(cfg) || n < 0) ? -1 : k_stats(cfg, n);
+    return (check_config(cfg) || n < 0 || n > kMaxTokens) ? -1 : k_stats(cfg, n);
 }
 int64_t kivi_v_code_words(const kivi_config* cfg, int64_t n) {
-    return (check_config(cfg) || n < 0) ? -1 : v_words(cfg, n);
+    return (check_config(cfg) || n < 0 || n > kMaxTokens) ? -1 : v_words(cfg, n);
 }
 int64_t kivi_v_stat_elems(const kivi_config* cfg, int64_t n) {
-    return (check_config(cfg) || n < 0) ? -1 : v_stats(cfg, n);
+    return (check_config(cfg) || n < 0 || n > kMaxTokens) ? -1 : v_stats(cfg, n);
 }
 int64_t kivi_ring_elems(const kivi_config* cfg) {
     return check_config(cfg) ? -1 : (int64_t(cfg->residual_length) + cfg->group_size) * cfg->head_dim;
@@ -736,9 +736,9 @@ int fp8_call(bool enc, const void* in, int64_t n_slices, int64_t n_tokens, int64
     if (in_stride % 16 != 0 || out_stride % 16 != 0) return KIVI_E_ALIGN;
     int64_t need = 0, total = 0;
     if (!mul_ok(n_tokens, D, &need) || in_stride < need || out_stride < need) return KIVI_E_SHAPE;
-    if (!mul_ok(n_slices, in_stride, &total) || !mul_ok(n_slices, out_stride, &total) ||
-        !mul_ok(total, 2, &total))
-        return KIVI_E_SHAPE;
+    // bytes of either array (fp16 on one side, one-byte codes on the other)
+    const int64_t wider = in_stride > out_stride ? in_stride : out_stride;
+    if (!mul_ok(n_slices, wider, &total) || !mul_ok(total, 2, &total)) return KIVI_E_SHAPE;
     if (!in || !out) return KIVI_E_NULL;
     if (!aligned16(in) || !aligned16(out)) return KIVI_E_ALIGN;
     kivi::Fp8Args a;

@@ -95,7 +95,8 @@ inline AttnPlan attn_plan(int64_t n_slices, int64_t n_quant, int64_t res_count) 
     p.n_blocks = (int32_t)((n_quant + 31) / 32);
     p.has_res = res_count > 0 ? 1 : 0;
     if (p.n_blocks > 0) {
-        int64_t want = n_slices > 0 ? (kTargetGroups + n_slices - 1) / n_slices : 1;
+        // workgroups per slice (at least 1; no overflow for any slice count)
+        int64_t want = n_slices >= kTargetGroups ? 1 : n_slices > 0 ? (kTargetGroups + n_slices - 1) / n_slices : 1;
         int64_t cap = (p.n_blocks + kMinBlocks - 1) / kMinBlocks;
         if (want > cap) want = cap;
         if (want < 1) want = 1;
