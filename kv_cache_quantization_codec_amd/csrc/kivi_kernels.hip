@@ -859,6 +859,18 @@ int value_lanes_log2(int G, int D) {
 
 constexpr int kValueRowsPerBlock = 64;
 
+// Occupancy caps of the decoders.  They write 2 bytes per element and read
+// about 0.4, and fewer resident workgroups (fewer concurrent write streams)
+// run faster: at the Llama-2-7B shape key decode takes 1.59 ms with at most
+// 3 workgroups per CU against 1.77 ms with the 8 its registers allow, value
+// decode 1.55 ms with at most 5 against 1.71 ms with 12 (Mistral-7B shape
+// 3.30 vs 3.59 and 3.56 vs 3.92 ms; outputs identical).  The launches
+// reserve LDS that the kernels do not use, which is what caps them: 3
+// workgroups of 53 KB, or 5 of 32 KB, fill the 160 KB of a CU.  The encoders
+// are read-bound and run fastest at full occupancy.
+constexpr size_t kDecodeKLdsCap = 53 * 1024;
+constexpr size_t kDecodeVLdsCap = 32 * 1024;
+
 template <int BITS, int G>
 int run_encode_k(const EncodeArgs& a, hipStream_t st) {
     const int D = a.head_dim;
@@ -911,7 +923,7 @@ int run_decode_k(const DecodeArgs& a, hipStream_t st) {
     const int64_t n_tiles = a.n_slices * ng;
     const int64_t nb = ceil_div64(n_tiles, tiles_pb);
     const int out_groups = (a.cap_tokens + G - 1) / G;
-    hipLaunchKernelGGL((decode_k_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), 0, st, a.codes,
+    hipLaunchKernelGGL((decode_k_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), kDecodeKLdsCap, st, a.codes,
                        a.scale, a.zero, a.n_tokens, D, ng, out_groups, tiles_pb, n_tiles, nb, a.out,
                        a.out_stride);
     return (int)hipGetLastError();
@@ -925,7 +937,7 @@ int run_decode_v(const DecodeArgs& a, hipStream_t st) {
     const int bps = (a.n_tokens + rpb - 1) / rpb;
     const int64_t nb = a.n_slices * bps;
     const int ngv = (D + G - 1) / G;
-    hipLaunchKernelGGL((decode_v_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), 0, st, a.codes,
+    hipLaunchKernelGGL((decode_v_kernel<BITS, G>), dim3(grid_for(nb)), dim3(kBlock), kDecodeVLdsCap, st, a.codes,
                        a.scale, a.zero, a.n_tokens, D, l2, bps, nb, a.cap_tokens, ngv, a.out,
                        a.out_stride);
     return (int)hipGetLastError();
