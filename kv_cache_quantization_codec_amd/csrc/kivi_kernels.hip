@@ -638,100 +638,427 @@ __device__ __forceinline__ void flush_keys(const StepArgs& a, int tpb, int64_t k
 }
 
 // Key flush of the usual step (all G tokens already in the ring, and the
-// group does not wrap around its end), with each channel pair split over a
-// lane pair: lanes 2q and 2q+1 of a slice's D lanes hold channels 2q, 2q+1
-// of tokens [0, G/2) and [G/2, G) of the group, exchange their partial
-// min/max with one DPP step, and each quantizes and packs its own half (a
-// half is a whole number of code words: G/2 is a multiple of 32/b).  Half
-// the registers of the one-lane-per-pair layout, so twice the resident
-// waves, each with half the work: 16,384 slices at G = 32 flush in 45 us
-// instead of 69 us (caches cold), with identical words.
-template <int BITS, int G>
-__device__ __forceinline__ void flush_keys_split(const StepArgs& a, int spb, int64_t kblk) {
-    constexpr int H = G / 2;
-    constexpr int W = G * BITS / 32;
-    constexpr int PER = 32 / BITS;
-    constexpr int HW = W / 2;                   // code words per half group
+// group does not wrap around its end).  A tile is spb slices; lane (j, c)
+// of a slice's (G/8) x (D/8) lanes holds channels 8c .. 8c+7 of tokens
+// [8j, 8j + 8) of the group as 8 16-byte row chunks, so each load
+// instruction of a wave reads whole rows.  The lanes of a channel chunk
+// then (1) combine their partial min/max, (2) derive each channel pair's
+// parameters once (lane j < 4 takes pair j) and share them, and (3) each
+// code their own 8 x 8 elements; at b = 2 a lane's 8 tokens are half a
+// code word, and each even lane ORs in its odd partner's upper halves.
+// With D = 128 and G = 32 a slice is one wave whose four token octets are
+// its four 16-lane rows, and all three exchanges are permlane swaps inside
+// the wave; other shapes exchange through LDS between barriers.  The
+// 16-byte loads and the short dependency chain are what matter: 16,384
+// slices (G = 32, D = 128) read their groups in 25 us with 16-byte loads
+// against 33 us with the 4-byte loads of a lane-per-channel-pair layout,
+// and coding through LDS took 38 us (caches cold).
+constexpr int kFlushTokensPerLane = 8;
+
+struct FlushParams {        // the 8 channels of one chunk
+    float rcp[8];
+    float nzr[8];
+    uint32_t sbits[4];      // fp16 scale pairs
+    uint32_t zbits[4];      // fp16 zero pairs
+};
+
+template <int NT>           // threads per block
+struct FlushLds {
+    union {
+        struct {
+            u32x4 mn[NT];   // partial minima, fp16 pairs of channels 8c .. 8c+7
+            u32x4 mx[NT];
+        } part;             // steps 1-2
+        u32x4 w[2][NT];     // upper half code words of odd lanes (b = 2), step 3
+    };
+    FlushParams prm[NT / 4];    // one per chunk (G/8 >= 4 lanes each)
+};
+
+// Workgroup barrier over LDS: this wave's LDS accesses complete, then the
+// barrier (global memory accesses are not waited for).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A lane's place in a flush tile.
+template <int G>
+struct FlushLane {
+    static constexpr int J = G / kFlushTokensPerLane;   // lanes per channel chunk
+    int cpr;        // chunks per row, D / 8
+    int P;          // lanes per slice
+    int si, j, c;   // slice in the tile, token octet, channel chunk
+    int chunk;      // chunk index in the tile
+    bool in_block;  // false for lanes past spb * P: they take part in the barriers only
+    __device__ FlushLane(int D, int spb) {
+        cpr = D >> 3;
+        P = J * cpr;
+        const int tid = threadIdx.x;
+        si = tid / P;
+        const int r = tid - si * P;
+        j = r / cpr;
+        c = r - j * cpr;
+        chunk = si * cpr + c;
+        in_block = si < spb;
+    }
+};
+
+// Slice of this lane in tile kt (lanes of slices past the end read slice
+// kt*spb, in bounds, and store nothing).
+template <int G>
+__device__ __forceinline__ int64_t flush_slice(const StepArgs& a, int spb, int64_t kt,
+                                               const FlushLane<G>& ln, bool& live) {
+    const int64_t s0 = kt * spb;
+    live = ln.in_block && s0 + ln.si < a.n_slices;
+    return s0 + (live ? ln.si : 0);
+}
+
+// Rows of tile kt through a buffer resource over the tile's slices: the
+// tile base is scalar, each lane keeps one 32-bit offset and the row step
+// is a scalar offset.
+template <int G>
+__device__ __forceinline__ void flush_load(const StepArgs& a, int spb, int64_t kt,
+                                           const FlushLane<G>& ln, u32x4 (&x)[kFlushTokensPerLane]) {
     const int D = a.head_dim;
-    const int si = threadIdx.x / D;             // slice within the block
-    const int l = threadIdx.x - si * D;
-    const int q = l >> 1, h = l & 1;            // channel pair, half
-    const int64_t s0 = kblk * spb;
-    const int64_t s = s0 + si;
-    // lanes past the block's slices load slice s0's rows (in bounds) and
-    // stop before storing; every lane takes part in the exchange
-    const bool live = si < spb && s < a.n_slices;
-    const int row_bytes = D * 2;
+    const int row_bytes = 2 * D;
+    const int64_t s0 = kt * spb;
     const int64_t nblk = (a.n_slices - s0 < spb) ? a.n_slices - s0 : spb;
     const __amdgpu_buffer_rsrc_t ring = buffer_rsrc(
         a.k_ring + s0 * a.ring_slots * (int64_t)D, (uint32_t)(nblk * a.ring_slots * row_bytes));
-    const int voff = ((live ? si : 0) * a.ring_slots * D + 2 * q) * 2 + h * H * row_bytes;
-    uint32_t v[H];
+    const int si = (ln.in_block && ln.si < nblk) ? ln.si : 0;
+    const int voff = (si * a.ring_slots + a.ring_head + kFlushTokensPerLane * ln.j) * row_bytes + 16 * ln.c;
 #pragma unroll
-    for (int i = 0; i < H; ++i)
-        v[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ring, voff, (a.ring_head + i) * row_bytes,
-                                                               kNontemporal);
-    f16x2 mn = as_h2(v[0]), mx = mn;
+    for (int i = 0; i < kFlushTokensPerLane; ++i)
+        x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ring, voff, i * row_bytes,
+                                                                               kNontemporal));
+}
+
+// Partial min/max of a lane's 8 channels (fp16 pairs) over its 8 tokens.
+__device__ __forceinline__ void flush_minmax(const u32x4 (&x)[kFlushTokensPerLane], f16x2 (&mn)[4],
+                                             f16x2 (&mx)[4]) {
 #pragma unroll
-    for (int i = 1; i < H; ++i) {
-        mn = pmin(mn, as_h2(v[i]));
-        mx = pmax(mx, as_h2(v[i]));
+    for (int k = 0; k < 4; ++k) mn[k] = mx[k] = as_h2(x[0][k]);
+#pragma unroll
+    for (int i = 1; i < kFlushTokensPerLane; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            mn[k] = pmin(mn[k], as_h2(x[i][k]));
+            mx[k] = pmax(mx[k], as_h2(x[i][k]));
+        }
+}
+
+// Parameters of one channel pair from its fp16 min/max pair.  A channel
+// outside the fast path gets 1/scale = 0, -zero/scale = 1/2: its y is then
+// 1/2 for every element, which always takes the exact branch of
+// flush_rows_code.
+template <int BITS>
+__device__ __forceinline__ void flush_pair_params(f16x2 mn, f16x2 mx, float& rcp0, float& rcp1,
+                                                  float& nzr0, float& nzr1, uint32_t& sbits,
+                                                  uint32_t& zbits) {
+    uint32_t s0b, z0b, s1b, z1b;
+    const QParams p0 = make_params<BITS>((float)mn.x, (float)mx.x, s0b, z0b);
+    const QParams p1 = make_params<BITS>((float)mn.y, (float)mx.y, s1b, z1b);
+    rcp0 = p0.fast ? p0.rcp : 0.0f;
+    rcp1 = p1.fast ? p1.rcp : 0.0f;
+    nzr0 = p0.fast ? p0.nzr : 0.5f;
+    nzr1 = p1.fast ? p1.nzr : 0.5f;
+    sbits = s0b | (s1b << 16);
+    zbits = z0b | (z1b << 16);
+}
+
+// Codes of a lane's 8 tokens x 8 channels, packed as they are made: at
+// b = 2 and 4 they accumulate in fp32 as sum(code * 2^(b*t)) over at most
+// 16 bits, which is exact; at b = 8 each goes into its byte with
+// v_cvt_pk_u8_f32.  Each row of 8 elements is coded branch-free and checked
+// once (its largest |y - rint(y)|); a row with an element within 2^-12 of a
+// rounding tie (see quant_fast), or of a channel outside the fast path, is
+// checked again element by element, and each such element gets its code
+// from the exact branch, which asks `bits(k)` for the fp16 scale and zero
+// pairs of channel pair k.  On random data about one row in five per wave
+// takes that branch.  w: b = 2, each channel's 16-bit half word in bits
+// 0-15; b = 4, one word; b = 8, two.
+template <int BITS, typename Bits>
+__device__ __forceinline__ void flush_rows_code(const u32x4 (&x)[kFlushTokensPerLane], const float (&rcp)[8],
+                                                const float (&nzr)[8], Bits bits,
+                                                uint32_t (&w)[8][BITS == 8 ? 2 : 1]) {
+    constexpr int NA = BITS == 4 ? 2 : 1;       // fp32 accumulators per channel (b = 2, 4)
+    float acc[8][NA];
+    uint32_t wb[8][2];                          // b = 8: code words of tokens 0-3, 4-7
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+#pragma unroll
+        for (int n = 0; n < NA; ++n) acc[m][n] = 0.0f;
+        wb[m][0] = wb[m][1] = 0;
     }
-    mn = pmin(mn, as_h2(dpp<0xB1>(as_u32(mn))));       // the partner lane's half
-    mx = pmax(mx, as_h2(dpp<0xB1>(as_u32(mx))));
-    if (!live) return;
-    uint32_t sb0, zb0, sb1, zb1;
-    const QParams p0 = make_params<BITS>((float)mn.x, (float)mx.x, sb0, zb0);
-    const QParams p1 = make_params<BITS>((float)mn.y, (float)mx.y, sb1, zb1);
-    uint32_t w0[HW], w1[HW];
+    // weight of token i's code in its accumulator
+    auto weight = [](int i) { return (float)(1u << (BITS == 8 ? 0 : BITS * (BITS == 4 ? (i & 3) : i))); };
 #pragma unroll
-    for (int w = 0; w < HW; ++w) {
-        w0[w] = 0;
-        w1[w] = 0;
-    }
-    bool redo = !(p0.fast && p1.fast);
-    if (!redo) {
+    for (int i = 0; i < kFlushTokensPerLane; ++i) {
         float worst = 0.0f;
 #pragma unroll
-        for (int t = 0; t < H; ++t) {
-            const float y0 = __builtin_fmaf(lo_f32(v[t]), p0.rcp, p0.nzr);
-            const float y1 = __builtin_fmaf(hi_f32(v[t]), p1.rcp, p1.nzr);
-            const float r0 = __builtin_rintf(y0);
-            const float r1 = __builtin_rintf(y1);
-            worst = __builtin_fmaxf(worst, __builtin_fmaxf(__builtin_fabsf(y0 - r0),
-                                                           __builtin_fabsf(y1 - r1)));
-            w0[t / PER] |= (uint32_t)r0 << ((t % PER) * BITS);
-            w1[t / PER] |= (uint32_t)r1 << ((t % PER) * BITS);
+        for (int m = 0; m < 8; ++m) {
+            const uint32_t xp = x[i][m >> 1];
+            const float xm = (m & 1) ? hi_f32(xp) : lo_f32(xp);
+            const float y = __builtin_fmaf(xm, rcp[m], nzr[m]);
+            const float rr = __builtin_rintf(y);
+            worst = __builtin_fmaxf(worst, __builtin_fabsf(y - rr));
+            if constexpr (BITS == 8)
+                wb[m][i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(rr, i & 3, wb[m][i >> 2]);
+            else
+                acc[m][BITS == 4 ? i >> 2 : 0] = __builtin_fmaf(rr, weight(i), acc[m][BITS == 4 ? i >> 2 : 0]);
         }
-        redo = worst > 0.5f - 0x1p-12f;
-    }
-    if (redo) {
+        if (__builtin_expect(worst > 0.5f - 0x1p-12f, 0)) {
 #pragma unroll
-        for (int w = 0; w < HW; ++w) {
-            w0[w] = 0;
-            w1[w] = 0;
+            for (int m = 0; m < 8; ++m) {
+                const uint32_t xp = x[i][m >> 1];
+                const float xm = (m & 1) ? hi_f32(xp) : lo_f32(xp);
+                const float y = __builtin_fmaf(xm, rcp[m], nzr[m]);
+                const float rr = __builtin_rintf(y);
+                if (__builtin_fabsf(y - rr) > 0.5f - 0x1p-12f) {
+                    uint32_t sb, zb;
+                    bits(m >> 1, sb, zb);
+                    QParams q;
+                    q.scale = (float)__builtin_bit_cast(f16, (uint16_t)(sb >> (16 * (m & 1))));
+                    q.zero = (float)__builtin_bit_cast(f16, (uint16_t)(zb >> (16 * (m & 1))));
+                    const float cm = (float)quant_exact<BITS>(xm, q);
+                    if constexpr (BITS == 8)
+                        wb[m][i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(cm, i & 3, wb[m][i >> 2]);
+                    else
+                        acc[m][BITS == 4 ? i >> 2 : 0] =
+                            __builtin_fmaf(cm - rr, weight(i), acc[m][BITS == 4 ? i >> 2 : 0]);
+                }
+            }
         }
+    }
 #pragma unroll
-        for (int t = 0; t < H; ++t) {
-            const float x0 = lo_f32(v[t]), x1 = hi_f32(v[t]);
-            const uint32_t c0 = p0.fast ? quant_fast<BITS>(x0, p0) : quant_exact<BITS>(x0, p0);
-            const uint32_t c1 = p1.fast ? quant_fast<BITS>(x1, p1) : quant_exact<BITS>(x1, p1);
-            w0[t / PER] |= c0 << ((t % PER) * BITS);
-            w1[t / PER] |= c1 << ((t % PER) * BITS);
+    for (int m = 0; m < 8; ++m) {
+        if constexpr (BITS == 8) {
+            w[m][0] = wb[m][0];
+            w[m][1] = wb[m][1];
+        } else if constexpr (BITS == 4) {
+            w[m][0] = (uint32_t)acc[m][0] | ((uint32_t)acc[m][1] << 16);
+        } else {
+            w[m][0] = (uint32_t)acc[m][0];
         }
     }
-    const int out_groups = a.cap_tokens / G;
-    const int64_t grp = s * out_groups + a.n_quant / G;
-    uint32_t* cdst = a.k_codes + grp * (int64_t)(W * D) + h * HW * D + 2 * q;
+}
+
+// Stores a lane's code words (b = 4, 8: all lanes; b = 2: the even lanes,
+// whose words already hold the odd partner's upper halves) and, from lane
+// j = 0 of each chunk, the chunk's sidecars.
+template <int BITS, int G>
+__device__ __forceinline__ void flush_store(const StepArgs& a, int64_t s, int j, int c,
+                                            const uint32_t (&w)[8][BITS == 8 ? 2 : 1],
+                                            const uint32_t (&sbits)[4], const uint32_t (&zbits)[4],
+                                            bool sidecars = true) {
+    constexpr int TW = kFlushTokensPerLane * BITS / 32;   // whole words per channel and lane (0: half)
+    constexpr int W = G * BITS / 32;
+    const int D = a.head_dim;
+    const int64_t grp = s * (a.cap_tokens / G) + a.n_quant / G;
+    uint32_t* cdst = a.k_codes + grp * (int64_t)(W * D) + 8 * c;
+    if constexpr (TW > 0) {
 #pragma unroll
-    for (int w = 0; w < HW; ++w)
-        __builtin_nontemporal_store(u32x2{w0[w], w1[w]}, reinterpret_cast<u32x2*>(cdst + w * D));
-    if (h == 0) {
-        __builtin_nontemporal_store(sb0 | (sb1 << 16),
-                                    reinterpret_cast<uint32_t*>(a.k_scale + grp * D + 2 * q));
-        __builtin_nontemporal_store(zb0 | (zb1 << 16),
-                                    reinterpret_cast<uint32_t*>(a.k_zero + grp * D + 2 * q));
+        for (int n = 0; n < TW; ++n) {
+            u32x4* dst = reinterpret_cast<u32x4*>(cdst + (int64_t)(j * TW + n) * D);
+            __builtin_nontemporal_store(u32x4{w[0][n], w[1][n], w[2][n], w[3][n]}, dst);
+            __builtin_nontemporal_store(u32x4{w[4][n], w[5][n], w[6][n], w[7][n]}, dst + 1);
+        }
+    } else if (!(j & 1)) {
+        u32x4* dst = reinterpret_cast<u32x4*>(cdst + (int64_t)(j >> 1) * D);
+        __builtin_nontemporal_store(u32x4{w[0][0], w[1][0], w[2][0], w[3][0]}, dst);
+        __builtin_nontemporal_store(u32x4{w[4][0], w[5][0], w[6][0], w[7][0]}, dst + 1);
     }
+    if (sidecars && j == 0) {
+        __builtin_nontemporal_store(u32x4{sbits[0], sbits[1], sbits[2], sbits[3]},
+                                    reinterpret_cast<u32x4*>(a.k_scale + grp * D + 8 * c));
+        __builtin_nontemporal_store(u32x4{zbits[0], zbits[1], zbits[2], zbits[3]},
+                                    reinterpret_cast<u32x4*>(a.k_zero + grp * D + 8 * c));
+    }
+}
+
+// Rows of lane (l & ~16) and (l | 16), then of lane (l & ~32) and (l | 32):
+// with D = 128 and G = 32 these are the same channel chunk's lanes in the
+// other token octets.
+__device__ __forceinline__ void swap16(uint32_t v, uint32_t& even, uint32_t& odd) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    even = r[0];
+    odd = r[1];
+}
+__device__ __forceinline__ void swap32(uint32_t v, uint32_t& lo, uint32_t& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    lo = r[0];
+    hi = r[1];
+}
+
+// One slice per wave, D = 128 and G = 32: lane l holds chunk c = l & 15 of
+// token octet j = l >> 4, and the chunk's four lanes are l ^ 16, l ^ 32,
+// l ^ 48.  Every exchange is a permlane swap; no LDS, no barrier.
+template <int BITS>
+__device__ __forceinline__ void flush_keys_wave(const StepArgs& a, int64_t s) {
+    static_assert(kFlushTokensPerLane == 8, "four token octets per 32-token group");
+    const int l = threadIdx.x & 63;
+    const int j = l >> 4, c = l & 15;
+    const bool live = s < a.n_slices;
+    const int64_t sl = live ? s : 0;
+    const int row_bytes = 256;
+    const __amdgpu_buffer_rsrc_t ring =
+        buffer_rsrc(a.k_ring + sl * a.ring_slots * (int64_t)128, (uint32_t)(a.ring_slots * row_bytes));
+    const int voff = (a.ring_head + 8 * j) * row_bytes + 16 * c;
+    u32x4 x[kFlushTokensPerLane];
+#pragma unroll
+    for (int i = 0; i < kFlushTokensPerLane; ++i)
+        x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ring, voff, i * row_bytes,
+                                                                               kNontemporal));
+    f16x2 mn[4], mx[4];
+    flush_minmax(x, mn, mx);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t e, o;
+        swap16(as_u32(mn[k]), e, o);
+        mn[k] = pmin(as_h2(e), as_h2(o));
+        swap32(as_u32(mn[k]), e, o);
+        mn[k] = pmin(as_h2(e), as_h2(o));
+        swap16(as_u32(mx[k]), e, o);
+        mx[k] = pmax(as_h2(e), as_h2(o));
+        swap32(as_u32(mx[k]), e, o);
+        mx[k] = pmax(as_h2(e), as_h2(o));
+    }
+    // lane j derives channel pair j, then the four rows' results are shared
+    const f16x2 pmn = j == 0 ? mn[0] : j == 1 ? mn[1] : j == 2 ? mn[2] : mn[3];
+    const f16x2 pmx = j == 0 ? mx[0] : j == 1 ? mx[1] : j == 2 ? mx[2] : mx[3];
+    float r0, r1, n0, n1;
+    uint32_t sb, zb;
+    flush_pair_params<BITS>(pmn, pmx, r0, r1, n0, n1, sb, zb);
+    float rcp[8], nzr[8];
+    uint32_t sbits[4], zbits[4];
+    // value v of row j -> out[row] for rows 0..3
+    auto share = [](uint32_t v, uint32_t (&out)[4]) {
+        uint32_t e, o;
+        swap16(v, e, o);               // rows (j & 2), (j | 1) of this half
+        swap32(e, out[0], out[2]);
+        swap32(o, out[1], out[3]);
+    };
+    {
+        uint32_t t[4];
+        share(__builtin_bit_cast(uint32_t, r0), t);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rcp[2 * k] = __builtin_bit_cast(float, t[k]);
+        share(__builtin_bit_cast(uint32_t, r1), t);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) rcp[2 * k + 1] = __builtin_bit_cast(float, t[k]);
+        share(__builtin_bit_cast(uint32_t, n0), t);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) nzr[2 * k] = __builtin_bit_cast(float, t[k]);
+        share(__builtin_bit_cast(uint32_t, n1), t);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) nzr[2 * k + 1] = __builtin_bit_cast(float, t[k]);
+        share(sb, sbits);
+        share(zb, zbits);
+    }
+    uint32_t w[8][BITS == 8 ? 2 : 1];
+    flush_rows_code<BITS>(x, rcp, nzr, [&](int k, uint32_t& sbk, uint32_t& zbk) {
+        sbk = sbits[k];
+        zbk = zbits[k];
+    }, w);
+    if (live) {
+        const int64_t grp = s * (a.cap_tokens / 32) + a.n_quant / 32;
+        if constexpr (BITS == 2) {
+            // rows j and j ^ 1 both hold word j >> 1 of the chunk (the odd
+            // row's half words as upper halves); each stores one half, so
+            // every store instruction writes whole 512-byte word rows
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                uint32_t e, o;
+                swap16(w[m][0], e, o);
+                w[m][0] = e | (o << 16);
+            }
+            const int h = j & 1;
+            uint32_t* dst = a.k_codes + grp * (int64_t)(2 * 128) + (j >> 1) * 128 + 8 * c + 4 * h;
+            __builtin_nontemporal_store(h ? u32x4{w[4][0], w[5][0], w[6][0], w[7][0]}
+                                          : u32x4{w[0][0], w[1][0], w[2][0], w[3][0]},
+                                        reinterpret_cast<u32x4*>(dst));
+        } else {
+            flush_store<BITS, 32>(a, s, j, c, w, sbits, zbits, false);
+        }
+        // sidecars: row 0 the scales, row 1 the zeros, one instruction
+        if (j < 2)
+            __builtin_nontemporal_store(
+                j ? u32x4{zbits[0], zbits[1], zbits[2], zbits[3]} : u32x4{sbits[0], sbits[1], sbits[2], sbits[3]},
+                reinterpret_cast<u32x4*>((j ? a.k_zero : a.k_scale) + grp * 128 + 8 * c));
+    }
+}
+
+// The general flush tile (spb slices, any D and G with (G/8) x (D/8) lanes
+// per slice within the block): the exchanges go through LDS.
+template <int BITS, int G, int NT>
+__device__ __forceinline__ void flush_keys_rows(const StepArgs& a, int spb, int64_t kt, FlushLds<NT>& sm) {
+    constexpr int J = FlushLane<G>::J;
+    const FlushLane<G> ln(a.head_dim, spb);
+    const int tid = threadIdx.x;
+    bool live;
+    const int64_t s = flush_slice<G>(a, spb, kt, ln, live);
+    u32x4 x[kFlushTokensPerLane];
+    flush_load<G>(a, spb, kt, ln, x);
+    {
+        f16x2 mn[4], mx[4];
+        flush_minmax(x, mn, mx);
+        if (ln.in_block) {
+            sm.part.mn[tid] = u32x4{as_u32(mn[0]), as_u32(mn[1]), as_u32(mn[2]), as_u32(mn[3])};
+            sm.part.mx[tid] = u32x4{as_u32(mx[0]), as_u32(mx[1]), as_u32(mx[2]), as_u32(mx[3])};
+        }
+    }
+    lds_barrier();
+    if (ln.in_block && ln.j < 4) {
+        const int base = ln.si * ln.P + ln.c;
+        const int j = ln.j;
+        const uint32_t* pmn = reinterpret_cast<const uint32_t*>(sm.part.mn);
+        const uint32_t* pmx = reinterpret_cast<const uint32_t*>(sm.part.mx);
+        f16x2 mn = as_h2(pmn[4 * base + j]), mx = as_h2(pmx[4 * base + j]);
+#pragma unroll 4
+        for (int jj = 1; jj < J; ++jj) {
+            mn = pmin(mn, as_h2(pmn[4 * (base + jj * ln.cpr) + j]));
+            mx = pmax(mx, as_h2(pmx[4 * (base + jj * ln.cpr) + j]));
+        }
+        FlushParams& fp = sm.prm[ln.chunk];
+        flush_pair_params<BITS>(mn, mx, fp.rcp[2 * j], fp.rcp[2 * j + 1], fp.nzr[2 * j], fp.nzr[2 * j + 1],
+                                fp.sbits[j], fp.zbits[j]);
+    }
+    lds_barrier();
+    const FlushParams& fp = sm.prm[ln.in_block ? ln.chunk : 0];
+    float rcp[8], nzr[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        rcp[m] = fp.rcp[m];
+        nzr[m] = fp.nzr[m];
+    }
+    uint32_t w[8][BITS == 8 ? 2 : 1];
+    flush_rows_code<BITS>(x, rcp, nzr, [&](int k, uint32_t& sbk, uint32_t& zbk) {
+        sbk = fp.sbits[k];
+        zbk = fp.zbits[k];
+    }, w);
+    if constexpr (BITS == 2) {
+        // step 1's space is free: every read of it came before the second barrier
+        if (ln.in_block && (ln.j & 1)) {
+            sm.w[0][tid] = u32x4{w[0][0], w[1][0], w[2][0], w[3][0]} << 16u;
+            sm.w[1][tid] = u32x4{w[4][0], w[5][0], w[6][0], w[7][0]} << 16u;
+        }
+        lds_barrier();
+        if (ln.in_block && !(ln.j & 1)) {
+            const u32x4 h0 = sm.w[0][tid + ln.cpr];
+            const u32x4 h1 = sm.w[1][tid + ln.cpr];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                w[k][0] |= h0[k];
+                w[4 + k][0] |= h1[k];
+            }
+        }
+    }
+    uint32_t sbits[4], zbits[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        sbits[k] = fp.sbits[k];
+        zbits[k] = fp.zbits[k];
+    }
+    if (live) flush_store<BITS, G>(a, s, ln.j, ln.c, w, sbits, zbits);
 }
 
 // Append of slice s (one token row, 2^lpt_log2 lanes of 8 channels): the new
@@ -741,13 +1068,13 @@ __device__ __forceinline__ void flush_keys_split(const StepArgs& a, int spb, int
 // store therefore already holds the codes of every residual value row (rows
 // past cap_tokens are skipped: they can never be flushed); only the key
 // groups wait for a flush.
-template <int BITS, int G>
+template <int BITS, int G, int NT = kBlock>
 __device__ __forceinline__ void append_row(const StepArgs& a, int64_t ablk, int lpt_log2) {
     constexpr int GL = G / 8;
     const int D = a.head_dim;
     const int lpt = 1 << lpt_log2;
     const int c = threadIdx.x & (lpt - 1);
-    const int64_t s0 = ablk * (kBlock >> lpt_log2) + (threadIdx.x >> lpt_log2);
+    const int64_t s0 = ablk * (NT >> lpt_log2) + (threadIdx.x >> lpt_log2);
     const bool svalid = s0 < a.n_slices;
     const int64_t s = svalid ? s0 : a.n_slices - 1;
     const bool cvalid = c < (D >> 3);
@@ -792,25 +1119,31 @@ append_flush_kernel(StepArgs a, int tpb, int lpt_log2, int64_t nk, int64_t na) {
 }
 
 // A flush step whose key group lies straight in the ring: block ranges
-// [0, nk) split key flush (spb slices per block), [nk, nk + na) appends.  A
-// kernel of its own, so that the one-lane-per-pair path's registers do not
-// limit these waves.
-template <int G>
-__global__ void __launch_bounds__(kBlock)
-append_flush_split_kernel(StepArgs a, int spb, int lpt_log2, int64_t nk) {
+// [0, nt) key flush tiles of spb slices (WAVE: one slice per wave, D = 128,
+// G = 32), [nt, nt + na) appends, NT threads per block.  Kernels of their
+// own, one per key width, so that neither the one-lane-per-pair path's
+// registers nor those of the other widths limit these waves.
+template <int KB, int G, int NT, bool WAVE>
+__global__ void __launch_bounds__(NT)
+append_flush_rows_kernel(StepArgs a, int spb, int lpt_log2, int64_t nt) {
     const int64_t b = blockIdx.x;
-    if (b < nk) {
-        switch (a.k_bits) {
-            case 2: flush_keys_split<2, G>(a, spb, b); break;
-            case 4: flush_keys_split<4, G>(a, spb, b); break;
-            default: flush_keys_split<8, G>(a, spb, b); break;
+    if (b < nt) {
+        if constexpr (WAVE) {
+            // the wave index is uniform over the wave; saying so keeps the
+            // slice's buffer resource in scalar registers (otherwise every
+            // load becomes a loop over the distinct resources of its lanes)
+            const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+            flush_keys_wave<KB>(a, b * (NT / 64) + wave);
+        } else {
+            __shared__ FlushLds<NT> sm;
+            flush_keys_rows<KB, G, NT>(a, spb, b, sm);
         }
         return;
     }
     switch (a.v_bits) {
-        case 2: append_row<2, G>(a, b - nk, lpt_log2); break;
-        case 4: append_row<4, G>(a, b - nk, lpt_log2); break;
-        default: append_row<8, G>(a, b - nk, lpt_log2); break;
+        case 2: append_row<2, G, NT>(a, b - nt, lpt_log2); break;
+        case 4: append_row<4, G, NT>(a, b - nt, lpt_log2); break;
+        default: append_row<8, G, NT>(a, b - nt, lpt_log2); break;
     }
 }
 
@@ -943,19 +1276,41 @@ int run_decode_v(const DecodeArgs& a, hipStream_t st) {
     return (int)hipGetLastError();
 }
 
+// Flush step from ring rows with NT threads per block.
+template <int KB, int G, int NT, bool WAVE>
+int launch_flush_rows(const StepArgs& a, int spb, int l2, int64_t nt, int64_t na, hipStream_t st) {
+    if (na + nt > 0x7FFFFFFF) return (int)hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((append_flush_rows_kernel<KB, G, NT, WAVE>), dim3((unsigned)(nt + na)), dim3(NT), 0, st,
+                       a, spb, l2, nt);
+    return (int)hipGetLastError();
+}
+
+template <int G, int NT, bool WAVE>
+int run_flush_rows(const StepArgs& a, int spb, hipStream_t st) {
+    const int l2 = value_lanes_log2(G, a.head_dim);
+    const int64_t nt = ceil_div64(a.n_slices, spb);
+    const int64_t na = ceil_div64(a.n_slices, NT >> l2);
+    if (a.k_bits == 2) return launch_flush_rows<2, G, NT, WAVE>(a, spb, l2, nt, na, st);
+    if (a.k_bits == 4) return launch_flush_rows<4, G, NT, WAVE>(a, spb, l2, nt, na, st);
+    return launch_flush_rows<8, G, NT, WAVE>(a, spb, l2, nt, na, st);
+}
+
 template <int G>
 int run_append_flush(const StepArgs& a, hipStream_t st) {
     const int D = a.head_dim;
     const int l2 = value_lanes_log2(G, D);
     const int64_t na = ceil_div64(a.n_slices, kBlock >> l2);
-    // the usual flush: all G tokens in the ring, not wrapping around its end
-    if (a.flush && a.ring_count >= G && a.ring_head + G <= a.ring_slots) {
-        const int spb = kBlock / D;
-        const int64_t nk = ceil_div64(a.n_slices, spb);
-        if (nk + na > 0x7FFFFFFF) return (int)hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((append_flush_split_kernel<G>), dim3((unsigned)(nk + na)), dim3(kBlock), 0, st,
-                           a, spb, l2, nk);
-        return (int)hipGetLastError();
+    // the usual flush: all G tokens in the ring, not wrapping around its end,
+    // and a slice's (G/8) x (D/8) lanes within one block (all but G = 128
+    // with D > 128).  D = 128 with G = 32 takes the wave-local path; other
+    // slices of at most one wave take one-wave workgroups, so that the waves
+    // never wait for each other at the LDS steps' barriers.
+    const int lanes = (G / kFlushTokensPerLane) * (D / 8);
+    if (a.flush && a.ring_count >= G && a.ring_head + G <= a.ring_slots && lanes <= kBlock) {
+        if constexpr (G == 32)
+            if (D == 128) return run_flush_rows<G, kBlock, true>(a, kBlock / 64, st);
+        return lanes <= 64 ? run_flush_rows<G, 64, false>(a, 64 / lanes, st)
+                           : run_flush_rows<G, kBlock, false>(a, kBlock / lanes, st);
     }
     const int tpb = key_tiles_per_block(D);
     const int64_t nk = a.flush ? ceil_div64(a.n_slices, tpb) : 0;

@@ -74,19 +74,28 @@ def test_stream_matches_oracle_every_flush(kb, vb, G, R, D, T0, steps):
     run_stream(kb, vb, G, R, D, T0, steps, S=6)
 
 
-# Flushes whose key group lies straight in the ring (R >= G, no wrap) split
-# each channel pair over two lanes, D lanes per slice and 256/D slices per
-# block; the others take one lane per pair.  These cases reach the split
-# layout's edges: idle lanes in a block (D = 96), eight slices per wave
-# (D = 8), 64-token halves (G = 128), 4- and 8-bit keys, a ring length that
-# alternates the two layouts (R = 40, G = 32: groups at slots 0, 32, then
-# 64..23 wrapping), and a partial last block (37 slices at D = 96).
+# Flushes whose key group lies straight in the ring (R >= G, no wrap) take
+# a lane per 8 channels and 8 tokens: (G/8) x (D/8) lanes per slice and
+# 256 / that many slices per block, unless a slice would need more than a
+# block (G = 128 with D > 128); the others take one lane per channel pair.
+# These cases reach the row layout's edges: idle lanes in a block (D = 96),
+# 64 slices per block (D = 8), half code words exchanged between lanes
+# (2-bit keys at G = 32, 64 and 128), 4- and 8-bit keys, a whole block per
+# slice (G = 128, D = 128; G = 64, D = 256), the fallback (G = 128,
+# D = 256), a ring length that alternates the two layouts (R = 40, G = 32:
+# groups at slots 0, 32, then 64..23 wrapping), and partial last blocks
+# (37 slices at D = 96, 5 at G = 64).
 SPLIT_CASES = [
     # k_bits, v_bits, G, R, D, prefill tokens, steps, slices
     (4, 2, 32, 64, 96, 100, 120, 6),
     (8, 4, 128, 128, 64, 300, 300, 6),
     (2, 8, 32, 40, 8, 50, 150, 6),
     (2, 2, 32, 32, 96, 70, 100, 37),
+    (2, 4, 64, 64, 128, 100, 140, 5),
+    (2, 2, 128, 128, 128, 200, 280, 3),
+    (4, 8, 128, 160, 64, 170, 300, 4),
+    (8, 2, 128, 128, 256, 140, 270, 3),
+    (2, 4, 32, 64, 256, 90, 100, 3),
 ]
 
 
@@ -95,12 +104,58 @@ def test_stream_split_flush_layouts(kb, vb, G, R, D, T0, steps, S):
     run_stream(kb, vb, G, R, D, T0, steps, S=S)
 
 
-def run_stream(kb, vb, G, R, D, T0, steps, S):
+def _adversarial_columns(S, T, D, seed):
+    """Keys whose channels run along the hard rows of the codec tests
+    (ties that a rounded reciprocal misleads, ranges on fp16 midpoints,
+    subnormal and zero scales, signed zeros, constants, the widest range),
+    one row per channel, cycled along tokens."""
+    from tests.test_gpu_parity import _adversarial_rows
+    rows = _adversarial_rows(D)
+    rng = np.random.default_rng(seed)
+    pick = rng.integers(0, rows.shape[0], size=(S, D))
+    t = np.arange(T) % rows.shape[1]
+    return np.stack([rows[pick[s]][:, t].T for s in range(S)]).astype(F16)
+
+
+# Keys with exact rounding ties and with the hard rows above, so that every
+# flush path takes its redo pass and its exact (non-fast) groups.
+ADVERSARIAL_CASES = [
+    # k_bits, v_bits, G, R, D, prefill tokens, steps, slices
+    (2, 2, 32, 128, 128, 160, 200, 5),
+    (4, 4, 64, 64, 96, 100, 200, 4),
+    (8, 2, 128, 128, 64, 140, 300, 3),
+    (2, 8, 32, 40, 64, 60, 140, 3),       # alternates with the one-lane-per-pair layout
+    (4, 2, 128, 128, 256, 130, 260, 2),   # the one-lane-per-pair layout only
+]
+
+
+@pytest.mark.parametrize("kind", ["ties", "rows"])
+@pytest.mark.parametrize("kb,vb,G,R,D,T0,steps,S", ADVERSARIAL_CASES)
+def test_stream_adversarial_keys(kind, kb, vb, G, R, D, T0, steps, S):
+    from kvsynth import uniform_with_ties
+
+    def data(rng):
+        T = T0 + steps
+        if kind == "ties":
+            k = uniform_with_ties(S, T, D, axis="token", n_valid=T, bits=kb, group_size=G,
+                                  seed=kb + G + D, grid_group_fraction=0.3, tie_fraction_in_group=0.25)
+        else:
+            k = _adversarial_columns(S, T, D, seed=kb + G + D)
+        v = uniform_with_ties(S, T, D, axis="channel", n_valid=T, bits=vb, group_size=G, seed=vb + G + D + 1)
+        return k, v
+
+    run_stream(kb, vb, G, R, D, T0, steps, S=S, data=data)
+
+
+def run_stream(kb, vb, G, R, D, T0, steps, S, data=None):
     print(f"stream kb={kb} vb={vb} G={G} R={R} D={D} T0={T0} steps={steps} S={S}", flush=True)
     sys.stdout.flush()
     rng = np.random.default_rng(kb * 100 + vb * 10 + G + R + D)
-    k_all = rng.standard_normal((S, T0 + steps, D)).astype(F16)
-    v_all = (rng.standard_normal((S, T0 + steps, D)) * 3).astype(F16)
+    if data is None:
+        k_all = rng.standard_normal((S, T0 + steps, D)).astype(F16)
+        v_all = (rng.standard_normal((S, T0 + steps, D)) * 3).astype(F16)
+    else:
+        k_all, v_all = data(rng)
     cap = -(-(T0 + steps) // G) * G
     cfg = K.Config(kb, vb, G, R, D)
     st = K.Stream(cfg, S, cap)
