@@ -647,8 +647,8 @@ __device__ __forceinline__ void flush_keys(const StepArgs& a, int tpb, int64_t k
 // code their own 8 x 8 elements; at b = 2 a lane's 8 tokens are half a
 // code word, and each even lane ORs in its odd partner's upper halves.
 // With D = 128 and G = 32 a slice is one wave whose four token octets are
-// its four 16-lane rows, and all three exchanges are permlane swaps inside
-// the wave; other shapes exchange through LDS between barriers.  The
+// its four 16-lane rows, and all three exchanges stay inside the wave;
+// other shapes exchange through LDS between workgroup barriers.  The
 // 16-byte loads and the short dependency chain are what matter: 16,384
 // slices (G = 32, D = 128) read their groups in 25 us with 16-byte loads
 // against 33 us with the 4-byte loads of a lane-per-channel-pair layout,
@@ -875,25 +875,25 @@ __device__ __forceinline__ void flush_store(const StepArgs& a, int64_t s, int j,
     }
 }
 
-// Rows of lane (l & ~16) and (l | 16), then of lane (l & ~32) and (l | 32):
-// with D = 128 and G = 32 these are the same channel chunk's lanes in the
-// other token octets.
-__device__ __forceinline__ void swap16(uint32_t v, uint32_t& even, uint32_t& odd) {
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    even = r[0];
-    odd = r[1];
-}
-__device__ __forceinline__ void swap32(uint32_t v, uint32_t& lo, uint32_t& hi) {
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    lo = r[0];
-    hi = r[1];
-}
+// LDS of one wave of the D = 128, G = 32 flush (16 channel chunks).
+struct FlushWaveLds {
+    u32x4 mn[64];           // partial min/max per lane; later the odd rows' half words
+    u32x4 mx[64];
+    float rcp[16][8];       // per chunk: its 8 channels' parameters
+    float nzr[16][8];
+    uint32_t sbits[16][4];
+    uint32_t zbits[16][4];
+};
 
 // One slice per wave, D = 128 and G = 32: lane l holds chunk c = l & 15 of
-// token octet j = l >> 4, and the chunk's four lanes are l ^ 16, l ^ 32,
-// l ^ 48.  Every exchange is a permlane swap; no LDS, no barrier.
+// token octet j = l >> 4, so the chunk's four lanes are c + 16r.  The
+// exchanges go through the wave's own LDS with no workgroup barrier: the
+// LDS accesses of one wave execute in order, and wave_barrier keeps the
+// compiler from moving them across the exchange points.  (Cross-lane
+// permlane swaps did the same work at about 32 cycles each; LDS traffic
+// also takes no VALU issue slots, which this kernel is short of.)
 template <int BITS>
-__device__ __forceinline__ void flush_keys_wave(const StepArgs& a, int64_t s) {
+__device__ __forceinline__ void flush_keys_wave(const StepArgs& a, int64_t s, FlushWaveLds& L) {
     static_assert(kFlushTokensPerLane == 8, "four token octets per 32-token group");
     const int l = threadIdx.x & 63;
     const int j = l >> 4, c = l & 15;
@@ -908,77 +908,64 @@ __device__ __forceinline__ void flush_keys_wave(const StepArgs& a, int64_t s) {
     for (int i = 0; i < kFlushTokensPerLane; ++i)
         x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ring, voff, i * row_bytes,
                                                                                kNontemporal));
-    f16x2 mn[4], mx[4];
-    flush_minmax(x, mn, mx);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t e, o;
-        swap16(as_u32(mn[k]), e, o);
-        mn[k] = pmin(as_h2(e), as_h2(o));
-        swap32(as_u32(mn[k]), e, o);
-        mn[k] = pmin(as_h2(e), as_h2(o));
-        swap16(as_u32(mx[k]), e, o);
-        mx[k] = pmax(as_h2(e), as_h2(o));
-        swap32(as_u32(mx[k]), e, o);
-        mx[k] = pmax(as_h2(e), as_h2(o));
+    {
+        f16x2 mn[4], mx[4];
+        flush_minmax(x, mn, mx);
+        L.mn[l] = u32x4{as_u32(mn[0]), as_u32(mn[1]), as_u32(mn[2]), as_u32(mn[3])};
+        L.mx[l] = u32x4{as_u32(mx[0]), as_u32(mx[1]), as_u32(mx[2]), as_u32(mx[3])};
     }
-    // lane j derives channel pair j, then the four rows' results are shared
-    const f16x2 pmn = j == 0 ? mn[0] : j == 1 ? mn[1] : j == 2 ? mn[2] : mn[3];
-    const f16x2 pmx = j == 0 ? mx[0] : j == 1 ? mx[1] : j == 2 ? mx[2] : mx[3];
-    float r0, r1, n0, n1;
-    uint32_t sb, zb;
-    flush_pair_params<BITS>(pmn, pmx, r0, r1, n0, n1, sb, zb);
+    __builtin_amdgcn_wave_barrier();
+    {
+        // lane j reduces channel pair j of its chunk over the four rows
+        const uint32_t* pmn = reinterpret_cast<const uint32_t*>(L.mn);
+        const uint32_t* pmx = reinterpret_cast<const uint32_t*>(L.mx);
+        f16x2 mn = as_h2(pmn[4 * c + j]), mx = as_h2(pmx[4 * c + j]);
+#pragma unroll
+        for (int r = 1; r < 4; ++r) {
+            mn = pmin(mn, as_h2(pmn[4 * (16 * r + c) + j]));
+            mx = pmax(mx, as_h2(pmx[4 * (16 * r + c) + j]));
+        }
+        flush_pair_params<BITS>(mn, mx, L.rcp[c][2 * j], L.rcp[c][2 * j + 1], L.nzr[c][2 * j],
+                                L.nzr[c][2 * j + 1], L.sbits[c][j], L.zbits[c][j]);
+    }
+    __builtin_amdgcn_wave_barrier();
     float rcp[8], nzr[8];
     uint32_t sbits[4], zbits[4];
-    // value v of row j -> out[row] for rows 0..3
-    auto share = [](uint32_t v, uint32_t (&out)[4]) {
-        uint32_t e, o;
-        swap16(v, e, o);               // rows (j & 2), (j | 1) of this half
-        swap32(e, out[0], out[2]);
-        swap32(o, out[1], out[3]);
-    };
-    {
-        uint32_t t[4];
-        share(__builtin_bit_cast(uint32_t, r0), t);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) rcp[2 * k] = __builtin_bit_cast(float, t[k]);
-        share(__builtin_bit_cast(uint32_t, r1), t);
+    for (int m = 0; m < 8; ++m) {
+        rcp[m] = L.rcp[c][m];
+        nzr[m] = L.nzr[c][m];
+    }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) rcp[2 * k + 1] = __builtin_bit_cast(float, t[k]);
-        share(__builtin_bit_cast(uint32_t, n0), t);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) nzr[2 * k] = __builtin_bit_cast(float, t[k]);
-        share(__builtin_bit_cast(uint32_t, n1), t);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) nzr[2 * k + 1] = __builtin_bit_cast(float, t[k]);
-        share(sb, sbits);
-        share(zb, zbits);
+    for (int k = 0; k < 4; ++k) {
+        sbits[k] = L.sbits[c][k];
+        zbits[k] = L.zbits[c][k];
     }
     uint32_t w[8][BITS == 8 ? 2 : 1];
     flush_rows_code<BITS>(x, rcp, nzr, [&](int k, uint32_t& sbk, uint32_t& zbk) {
         sbk = sbits[k];
         zbk = zbits[k];
     }, w);
+    if constexpr (BITS == 2) {
+        // odd rows post their half words as upper halves, in step 1's space
+        // (its last reads came before the previous exchange point)
+        if (j & 1) {
+            L.mn[l] = u32x4{w[0][0], w[1][0], w[2][0], w[3][0]} << 16u;
+            L.mx[l] = u32x4{w[4][0], w[5][0], w[6][0], w[7][0]} << 16u;
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (!(j & 1)) {
+            const u32x4 h0 = L.mn[l + 16], h1 = L.mx[l + 16];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                w[k][0] |= h0[k];
+                w[4 + k][0] |= h1[k];
+            }
+        }
+    }
     if (live) {
         const int64_t grp = s * (a.cap_tokens / 32) + a.n_quant / 32;
-        if constexpr (BITS == 2) {
-            // rows j and j ^ 1 both hold word j >> 1 of the chunk (the odd
-            // row's half words as upper halves); each stores one half, so
-            // every store instruction writes whole 512-byte word rows
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                uint32_t e, o;
-                swap16(w[m][0], e, o);
-                w[m][0] = e | (o << 16);
-            }
-            const int h = j & 1;
-            uint32_t* dst = a.k_codes + grp * (int64_t)(2 * 128) + (j >> 1) * 128 + 8 * c + 4 * h;
-            __builtin_nontemporal_store(h ? u32x4{w[4][0], w[5][0], w[6][0], w[7][0]}
-                                          : u32x4{w[0][0], w[1][0], w[2][0], w[3][0]},
-                                        reinterpret_cast<u32x4*>(dst));
-        } else {
-            flush_store<BITS, 32>(a, s, j, c, w, sbits, zbits, false);
-        }
+        flush_store<BITS, 32>(a, s, j, c, w, sbits, zbits, false);
         // sidecars: row 0 the scales, row 1 the zeros, one instruction
         if (j < 2)
             __builtin_nontemporal_store(
@@ -1129,11 +1116,12 @@ append_flush_rows_kernel(StepArgs a, int spb, int lpt_log2, int64_t nt) {
     const int64_t b = blockIdx.x;
     if (b < nt) {
         if constexpr (WAVE) {
+            __shared__ FlushWaveLds sw[NT / 64];
             // the wave index is uniform over the wave; saying so keeps the
             // slice's buffer resource in scalar registers (otherwise every
             // load becomes a loop over the distinct resources of its lanes)
             const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-            flush_keys_wave<KB>(a, b * (NT / 64) + wave);
+            flush_keys_wave<KB>(a, b * (NT / 64) + wave, sw[wave]);
         } else {
             __shared__ FlushLds<NT> sm;
             flush_keys_rows<KB, G, NT>(a, spb, b, sm);
