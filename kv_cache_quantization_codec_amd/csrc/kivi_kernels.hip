@@ -198,19 +198,45 @@ __device__ __forceinline__ void key_column(Load load, int nv, int D, int p, int6
     }
     bool redo = !(p0.fast && p1.fast);
     if (!redo) {
+        // Codes are packed as they are made: at b = 2 and 4 they accumulate
+        // in fp32 as sum(code * 2^(b*k)) over 16-bit half words (exact),
+        // one fma each instead of a conversion, a shift and an OR; at b = 8
+        // each goes into its byte with v_cvt_pk_u8_f32.
+        constexpr int TH = BITS == 8 ? 2 : 16 / BITS;     // tokens per 16-bit half word
+        float h0[2 * W], h1[2 * W];
+#pragma unroll
+        for (int k = 0; k < 2 * W; ++k) {
+            h0[k] = 0.0f;
+            h1[k] = 0.0f;
+        }
         float worst = 0.0f;
 #pragma unroll
         for (int t = 0; t < G; ++t) {
             const float y0 = __builtin_fmaf(lo_f32(v[t]), p0.rcp, p0.nzr);
             const float y1 = __builtin_fmaf(hi_f32(v[t]), p1.rcp, p1.nzr);
-            const float r0 = __builtin_rintf(y0);
-            const float r1 = __builtin_rintf(y1);
+            float r0 = __builtin_rintf(y0);
+            float r1 = __builtin_rintf(y1);
             worst = __builtin_fmaxf(worst, __builtin_fmaxf(__builtin_fabsf(y0 - r0),
                                                            __builtin_fabsf(y1 - r1)));
-            const uint32_t c0 = (!FULL && t >= nv) ? 0u : (uint32_t)r0;
-            const uint32_t c1 = (!FULL && t >= nv) ? 0u : (uint32_t)r1;
-            w0[t / PER] |= c0 << ((t % PER) * BITS);
-            w1[t / PER] |= c1 << ((t % PER) * BITS);
+            if (!FULL && t >= nv) {
+                r0 = 0.0f;
+                r1 = 0.0f;
+            }
+            if constexpr (BITS == 8) {
+                w0[t / PER] = __builtin_amdgcn_cvt_pk_u8_f32(r0, t % PER, w0[t / PER]);
+                w1[t / PER] = __builtin_amdgcn_cvt_pk_u8_f32(r1, t % PER, w1[t / PER]);
+            } else {
+                const float wt = (float)(1u << (BITS * (t % TH)));
+                h0[t / TH] = __builtin_fmaf(r0, wt, h0[t / TH]);
+                h1[t / TH] = __builtin_fmaf(r1, wt, h1[t / TH]);
+            }
+        }
+        if constexpr (BITS != 8) {
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                w0[w] = (uint32_t)h0[2 * w] | ((uint32_t)h0[2 * w + 1] << 16);
+                w1[w] = (uint32_t)h1[2 * w] | ((uint32_t)h1[2 * w + 1] << 16);
+            }
         }
         redo = worst > 0.5f - 0x1p-12f;
     }
