@@ -126,28 +126,29 @@ __device__ __forceinline__ uint32_t quant_fast(float x, const QParams& p) {
     return q;
 }
 
-// Codes of N elements x(i) of one group.  Fast groups take a branch-free
+// Codes of N elements x(i) of one group, as floats (exact small integers,
+// ready for packing by fp32 accumulation).  Fast groups take a branch-free
 // pass that also records the largest |y - rint(y)|; only when some element
 // came within 2^-12 of a half-integer (rare) is the pass redone with the
 // per-element check of quant_fast.
 template <int BITS, int N, typename X>
-__device__ __forceinline__ void quant_n(X x, const QParams& p, uint32_t* q) {
+__device__ __forceinline__ void quant_n(X x, const QParams& p, float* q) {
     if (p.fast) {
         float worst = 0.0f;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const float y = __builtin_fmaf(x(i), p.rcp, p.nzr);
             const float r = __builtin_rintf(y);
-            q[i] = (uint32_t)r;
+            q[i] = r;
             worst = __builtin_fmaxf(worst, __builtin_fabsf(y - r));
         }
         if (worst > 0.5f - 0x1p-12f) {
 #pragma unroll
-            for (int i = 0; i < N; ++i) q[i] = quant_fast<BITS>(x(i), p);
+            for (int i = 0; i < N; ++i) q[i] = (float)quant_fast<BITS>(x(i), p);
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < N; ++i) q[i] = quant_exact<BITS>(x(i), p);
+        for (int i = 0; i < N; ++i) q[i] = (float)quant_exact<BITS>(x(i), p);
     }
 }
 
@@ -196,39 +197,74 @@ __device__ __forceinline__ void key_column(Load load, int nv, int D, int p, int6
         w0[w] = 0;
         w1[w] = 0;
     }
-    bool redo = !(p0.fast && p1.fast);
-    if (!redo) {
+    if (p0.fast && p1.fast) {
         // Codes are packed as they are made: at b = 2 and 4 they accumulate
         // in fp32 as sum(code * 2^(b*k)) over 16-bit half words (exact),
         // one fma each instead of a conversion, a shift and an OR; at b = 8
-        // each goes into its byte with v_cvt_pk_u8_f32.
+        // each goes into its byte with v_cvt_pk_u8_f32.  Near-ties (see
+        // quant_fast) are tracked per segment of 4 tokens, and only flagged
+        // segments are checked again element by element: with 64 lanes x
+        // 64 elements per wave, most waves hold some element within 2^-12 of
+        // a tie, so a second pass over whole lanes would run in most waves.
         constexpr int TH = BITS == 8 ? 2 : 16 / BITS;     // tokens per 16-bit half word
+        constexpr int SEG = 4;                            // tokens per near-tie segment
+        constexpr float kNear = 0.5f - 0x1p-12f;
         float h0[2 * W], h1[2 * W];
 #pragma unroll
         for (int k = 0; k < 2 * W; ++k) {
             h0[k] = 0.0f;
             h1[k] = 0.0f;
         }
-        float worst = 0.0f;
-#pragma unroll
-        for (int t = 0; t < G; ++t) {
-            const float y0 = __builtin_fmaf(lo_f32(v[t]), p0.rcp, p0.nzr);
-            const float y1 = __builtin_fmaf(hi_f32(v[t]), p1.rcp, p1.nzr);
-            float r0 = __builtin_rintf(y0);
-            float r1 = __builtin_rintf(y1);
-            worst = __builtin_fmaxf(worst, __builtin_fmaxf(__builtin_fabsf(y0 - r0),
-                                                           __builtin_fabsf(y1 - r1)));
-            if (!FULL && t >= nv) {
-                r0 = 0.0f;
-                r1 = 0.0f;
-            }
+        auto put = [&](int t, float c0, float c1) {
             if constexpr (BITS == 8) {
-                w0[t / PER] = __builtin_amdgcn_cvt_pk_u8_f32(r0, t % PER, w0[t / PER]);
-                w1[t / PER] = __builtin_amdgcn_cvt_pk_u8_f32(r1, t % PER, w1[t / PER]);
+                w0[t / PER] = __builtin_amdgcn_cvt_pk_u8_f32(c0, t % PER, w0[t / PER]);
+                w1[t / PER] = __builtin_amdgcn_cvt_pk_u8_f32(c1, t % PER, w1[t / PER]);
             } else {
                 const float wt = (float)(1u << (BITS * (t % TH)));
-                h0[t / TH] = __builtin_fmaf(r0, wt, h0[t / TH]);
-                h1[t / TH] = __builtin_fmaf(r1, wt, h1[t / TH]);
+                h0[t / TH] = __builtin_fmaf(c0, wt, h0[t / TH]);
+                h1[t / TH] = __builtin_fmaf(c1, wt, h1[t / TH]);
+            }
+        };
+#pragma unroll
+        for (int sg = 0; sg < G / SEG; ++sg) {
+            float worst = 0.0f;
+#pragma unroll
+            for (int t = SEG * sg; t < SEG * sg + SEG; ++t) {
+                const float y0 = __builtin_fmaf(lo_f32(v[t]), p0.rcp, p0.nzr);
+                const float y1 = __builtin_fmaf(hi_f32(v[t]), p1.rcp, p1.nzr);
+                float r0 = __builtin_rintf(y0);
+                float r1 = __builtin_rintf(y1);
+                if (FULL || t < nv) {
+                    worst = __builtin_fmaxf(worst, __builtin_fmaxf(__builtin_fabsf(y0 - r0),
+                                                                   __builtin_fabsf(y1 - r1)));
+                } else {
+                    r0 = 0.0f;
+                    r1 = 0.0f;
+                }
+                put(t, r0, r1);
+            }
+            if (__builtin_expect(worst > kNear, 0)) {
+#pragma unroll
+                for (int t = SEG * sg; t < SEG * sg + SEG; ++t) {
+                    if (!FULL && t >= nv) continue;
+#pragma unroll
+                    for (int ch = 0; ch < 2; ++ch) {
+                        const QParams& q = ch ? p1 : p0;
+                        const float x = ch ? hi_f32(v[t]) : lo_f32(v[t]);
+                        const float y = __builtin_fmaf(x, q.rcp, q.nzr);
+                        const float rr = __builtin_rintf(y);
+                        if (__builtin_fabsf(y - rr) > kNear) {
+                            const float c = (float)quant_exact<BITS>(x, q);
+                            if constexpr (BITS == 8) {
+                                uint32_t& wd = ch ? w1[t / PER] : w0[t / PER];
+                                wd = __builtin_amdgcn_cvt_pk_u8_f32(c, t % PER, wd);
+                            } else {
+                                float& hk = ch ? h1[t / TH] : h0[t / TH];
+                                hk = __builtin_fmaf(c - rr, (float)(1u << (BITS * (t % TH))), hk);
+                            }
+                        }
+                    }
+                }
             }
         }
         if constexpr (BITS != 8) {
@@ -238,14 +274,9 @@ __device__ __forceinline__ void key_column(Load load, int nv, int D, int p, int6
                 w1[w] = (uint32_t)h1[2 * w] | ((uint32_t)h1[2 * w + 1] << 16);
             }
         }
-        redo = worst > 0.5f - 0x1p-12f;
-    }
-    if (redo) {
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            w0[w] = 0;
-            w1[w] = 0;
-        }
+    } else {
+        // a channel outside the fast path: every element by the definition
+        // (or by quant_fast for the other channel)
 #pragma unroll
         for (int t = 0; t < G; ++t) {
             const float x0 = lo_f32(v[t]), x1 = hi_f32(v[t]);
@@ -392,26 +423,37 @@ __device__ __forceinline__ void value_chunk(const u32x4& x, bool cvalid, int c, 
     uint32_t sb, zb;
     const QParams prm = make_params<BITS>((float)pr.x, -(float)pr.y, sb, zb);
     const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
-    uint32_t q[8];
+    float q[8];
     quant_n<BITS, 8>([&](int i) { return (i & 1) ? hi_f32(xs[i >> 1]) : lo_f32(xs[i >> 1]); }, prm, q);
     if (!ALL && !cvalid) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = 0;
+        for (int i = 0; i < 8; ++i) q[i] = 0.0f;
     }
+    // codes packed by fp32 accumulation over 16-bit half words (exact), or
+    // into bytes with v_cvt_pk_u8_f32
     if (BITS == 4) {
-        uint32_t w = 0;
+        float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w |= q[i] << (4 * i);
+        for (int i = 0; i < 4; ++i) {
+            a0 = __builtin_fmaf(q[i], (float)(1u << (4 * i)), a0);
+            a1 = __builtin_fmaf(q[4 + i], (float)(1u << (4 * i)), a1);
+        }
+        const uint32_t w = (uint32_t)a0 | ((uint32_t)a1 << 16);
         if (store) __builtin_nontemporal_store(w, row_codes + c);
     } else if (BITS == 8) {
-        const uint32_t w0 = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-        const uint32_t w1 = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w0 = __builtin_amdgcn_cvt_pk_u8_f32(q[i], i, w0);
+            w1 = __builtin_amdgcn_cvt_pk_u8_f32(q[4 + i], i, w1);
+        }
         if (store)
             __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(row_codes + 2 * c));
     } else {
-        uint32_t h = 0;
+        float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h |= q[i] << (2 * i);
+        for (int i = 0; i < 8; ++i) a = __builtin_fmaf(q[i], (float)(1u << (2 * i)), a);
+        const uint32_t h = (uint32_t)a;
         const uint32_t nb = dpp<0xB1>(h);
         if (store && (c & 1) == 0) __builtin_nontemporal_store(h | (nb << 16), row_codes + (c >> 1));
     }
