@@ -668,6 +668,134 @@ decode_v_kernel(const uint32_t* __restrict__ codes, const uint16_t* __restrict__
     }
 }
 
+// Value encode at G = 32 when every lane of a row holds 8 channels of a
+// stored group (D % 32 == 0, D/8 lanes per row): each lane takes 4 rows,
+// r0 + k*rstep for k = 0..3.  A group is a quad of lanes, and after the
+// quad's min/max reduction all four lanes know the statistics of all four
+// rows' groups; lane e of the quad derives the parameters of row e's group
+// only and the quad broadcasts them back (DPP), so each group's parameters
+// cost one lane instead of four: the encoder is short of VALU issue
+// slots, not of bandwidth.  Codes as in value_chunk; rows past n_tokens are
+// coded from zeros and not stored.
+template <int K>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, K * 0x55, 0xF, 0xF, false);
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(kBlock)
+encode_v_quad_kernel(const uint16_t* __restrict__ in, int64_t in_stride, int n_tokens, int D, int lpt_log2,
+                     int blocks_per_slice, int64_t n_blocks, uint32_t* __restrict__ codes,
+                     uint16_t* __restrict__ scale, uint16_t* __restrict__ zero, int cap) {
+    constexpr int G = 32;
+    const int lpt = 1 << lpt_log2;
+    const int c = threadIdx.x & (lpt - 1);
+    const int r0 = threadIdx.x >> lpt_log2;
+    const int rstep = kBlock >> lpt_log2;
+    const int rows_per_block = 4 * rstep;
+    const int e = c & 3, gq = c >> 2;
+    const int ngv = D / G;
+    const int wpt = D * BITS / 32;
+    for (int64_t blk = xcd_block<128>(); blk < n_blocks; blk += gridDim.x) {
+        const int64_t s = blk / blocks_per_slice;
+        const int tb = (int)(blk - s * blocks_per_slice) * rows_per_block + r0;
+        const uint16_t* src = in + s * in_stride;
+        u32x4 x[4];
+        uint32_t pr[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int t = tb + k * rstep;
+            x[k] = u32x4{0, 0, 0, 0};
+            if (t < n_tokens)
+                x[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (int64_t)t * D + 8 * c));
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const f16x2 a0 = as_h2(x[k].x), a1 = as_h2(x[k].y), a2 = as_h2(x[k].z), a3 = as_h2(x[k].w);
+            const f16x2 mn2 = pmin(pmin(a0, a1), pmin(a2, a3));
+            const f16x2 mx2 = pmax(pmax(a0, a1), pmax(a2, a3));
+            f16x2 p2;
+            p2.x = mn2.x < mn2.y ? mn2.x : mn2.y;
+            p2.y = -(mx2.x > mx2.y ? mx2.x : mx2.y);
+            uint32_t pu = as_u32(p2);
+            pu = as_u32(pmin(as_h2(pu), as_h2(dpp<0xB1>(pu))));
+            pr[k] = as_u32(pmin(as_h2(pu), as_h2(dpp<0x4E>(pu))));
+        }
+        // lane e: the parameters of row e's group
+        const f16x2 pe = as_h2(e == 0 ? pr[0] : e == 1 ? pr[1] : e == 2 ? pr[2] : pr[3]);
+        uint32_t sb, zb;
+        const QParams prm = make_params<BITS>((float)pe.x, -(float)pe.y, sb, zb);
+        // outside the fast path: 1/scale = 0, -zero/scale = 1/2, so that
+        // every element takes the exact branch below
+        const uint32_t rcp_e = __builtin_bit_cast(uint32_t, prm.fast ? prm.rcp : 0.0f);
+        const uint32_t nzr_e = __builtin_bit_cast(uint32_t, prm.fast ? prm.nzr : 0.5f);
+        const uint32_t sz_e = sb | (zb << 16);
+        {
+            const int te = tb + e * rstep;
+            if (te < n_tokens) {
+                const int64_t row = s * cap + te;
+                scale[row * ngv + gq] = (uint16_t)sb;
+                zero[row * ngv + gq] = (uint16_t)zb;
+            }
+        }
+        auto code_row = [&](int k, uint32_t rcpb, uint32_t nzrb, uint32_t sz) {
+            const float rcp = __builtin_bit_cast(float, rcpb), nzr = __builtin_bit_cast(float, nzrb);
+            const uint32_t xs[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+            auto xv = [&](int i) { return (i & 1) ? hi_f32(xs[i >> 1]) : lo_f32(xs[i >> 1]); };
+            float q[8];
+            float worst = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float y = __builtin_fmaf(xv(i), rcp, nzr);
+                q[i] = __builtin_rintf(y);
+                worst = __builtin_fmaxf(worst, __builtin_fabsf(y - q[i]));
+            }
+            if (__builtin_expect(worst > 0.5f - 0x1p-12f, 0)) {
+                QParams qp;
+                qp.scale = (float)__builtin_bit_cast(f16, (uint16_t)(sz & 0xFFFFu));
+                qp.zero = (float)__builtin_bit_cast(f16, (uint16_t)(sz >> 16));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float y = __builtin_fmaf(xv(i), rcp, nzr);
+                    if (__builtin_fabsf(y - q[i]) > 0.5f - 0x1p-12f) q[i] = (float)quant_exact<BITS>(xv(i), qp);
+                }
+            }
+            const int t = tb + k * rstep;
+            const bool store = t < n_tokens;
+            uint32_t* row_codes = codes + (s * cap + t) * (int64_t)wpt;
+            if (BITS == 4) {
+                float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a0 = __builtin_fmaf(q[i], (float)(1u << (4 * i)), a0);
+                    a1 = __builtin_fmaf(q[4 + i], (float)(1u << (4 * i)), a1);
+                }
+                if (store) __builtin_nontemporal_store((uint32_t)a0 | ((uint32_t)a1 << 16), row_codes + c);
+            } else if (BITS == 8) {
+                uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    w0 = __builtin_amdgcn_cvt_pk_u8_f32(q[i], i, w0);
+                    w1 = __builtin_amdgcn_cvt_pk_u8_f32(q[4 + i], i, w1);
+                }
+                if (store)
+                    __builtin_nontemporal_store(u32x2{w0, w1}, reinterpret_cast<u32x2*>(row_codes + 2 * c));
+            } else {
+                float a = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a = __builtin_fmaf(q[i], (float)(1u << (2 * i)), a);
+                const uint32_t h = (uint32_t)a;
+                const uint32_t nb = dpp<0xB1>(h);
+                if (store && (c & 1) == 0) __builtin_nontemporal_store(h | (nb << 16), row_codes + (c >> 1));
+            }
+        };
+        code_row(0, quad_bcast<0>(rcp_e), quad_bcast<0>(nzr_e), quad_bcast<0>(sz_e));
+        code_row(1, quad_bcast<1>(rcp_e), quad_bcast<1>(nzr_e), quad_bcast<1>(sz_e));
+        code_row(2, quad_bcast<2>(rcp_e), quad_bcast<2>(nzr_e), quad_bcast<2>(sz_e));
+        code_row(3, quad_bcast<3>(rcp_e), quad_bcast<3>(nzr_e), quad_bcast<3>(sz_e));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // streaming: append one token per slice, optionally flush the oldest G
 // ---------------------------------------------------------------------------
@@ -1293,7 +1421,13 @@ int run_encode_v(const EncodeArgs& a, hipStream_t st) {
     const int64_t nb = a.n_slices * bps;
     const int ngv = (D + G - 1) / G;
     const bool all = (1 << l2) == D / 8 && D % G == 0;
-    if (all)
+    if (G == 32 && all) {
+        const int rows_per_block = 4 * (kBlock >> l2);
+        const int bpq = (a.n_tokens + rows_per_block - 1) / rows_per_block;
+        const int64_t nq = a.n_slices * bpq;
+        hipLaunchKernelGGL((encode_v_quad_kernel<BITS>), dim3(grid_for(nq)), dim3(kBlock), 0, st, a.in,
+                           a.in_stride, a.n_tokens, D, l2, bpq, nq, a.codes, a.scale, a.zero, a.cap_tokens);
+    } else if (all)
         hipLaunchKernelGGL((encode_v_kernel<BITS, G, true>), dim3(grid_for(nb)), dim3(kBlock), 0,
                            st, a.in, a.in_stride, a.n_tokens, D, l2, kValueRowsPerBlock, bps, nb,
                            a.codes, a.scale, a.zero, a.cap_tokens, ngv);

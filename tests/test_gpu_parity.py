@@ -79,7 +79,7 @@ def test_xcd_ordered_grids_with_tails(b):
 
 
 @pytest.mark.parametrize("kind", ["k", "v"])
-@pytest.mark.parametrize("D,G", [(128, 32), (96, 64), (64, 128), (8, 32), (256, 128), (40, 32)])
+@pytest.mark.parametrize("D,G", [(128, 32), (96, 64), (64, 128), (8, 32), (256, 128), (40, 32), (256, 32), (32, 32)])
 def test_strided_input_and_capacity(kind, D, G):
     rng = np.random.default_rng(D + G)
     S, T, n = 5, 300, 211
@@ -93,9 +93,9 @@ def test_strided_input_and_capacity(kind, D, G):
 @pytest.mark.parametrize("kind", ["k", "v"])
 def test_tiny_counts(kind):
     rng = np.random.default_rng(3)
-    for n in (1, 2, 31, 32, 33, 63, 65):
+    for n in (1, 2, 31, 32, 33, 63, 65, 129, 255, 257):
         x = rng.standard_normal((3, n, 64)).astype(F16)
-        for b, G in ((2, 32), (4, 64), (8, 128)):
+        for b, G in ((2, 32), (4, 64), (8, 128), (4, 32), (8, 32)):
             U.check_round_trip(kind, K.Config(b, b, G, 0, 64), x, n)
 
 
