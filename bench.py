@@ -87,10 +87,12 @@ CODEC_KERNELS = ("encode_k", "encode_v", "decode_k", "decode_v")
 
 
 def _codec_kernel(name: str):
-    """Which codec kernel a rocprofv3 kernel name is, or None."""
+    """Which codec kernel a rocprofv3 kernel name is, or None (value encode
+    at G = 32 launches encode_v_quad_kernel)."""
     for k in CODEC_KERNELS:
-        if f"kivi::(anonymous namespace)::{k}_kernel<" in name:
-            return k
+        for form in (f"{k}_kernel<", f"{k}_quad_kernel<"):
+            if f"kivi::(anonymous namespace)::{form}" in name:
+                return k
     return None
 
 
