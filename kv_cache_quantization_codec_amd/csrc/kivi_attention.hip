@@ -33,16 +33,20 @@
 //   whole consecutive token rows (a code unit is one word column of tokens
 //   p, p + 16, p + 8, p + 24); the value product's token order follows the
 //   units (vslot), and the weight operands are written in that order.
-// * Three kernel variants by the bound on query heads per KV slice (2, 4,
-//   8) size the LDS operand rows.  Lane rows of the value-weight step that
-//   hold no head take a share of the value groups.  The variants for 3-8
-//   heads run a slice's full 32-token blocks without per-token bounds; the
-//   1-2 head variant keeps one loop (its registers and code size decide).
+// * Four kernel variants by the bound on query heads per KV slice (1, 2,
+//   4, 8) size the LDS operand rows and drop the second head of a lane row
+//   where there is none.  Lane rows of the value-weight step that hold no
+//   head take a share of the value groups; with 1-2 heads the key-score
+//   operand rows repeat in every group of four MFMA rows, so every lane row
+//   has the weights without a cross-lane copy.  A slice's full 32-token
+//   blocks run without per-token bounds; only its last block can be partial.
 // * The logit scale is folded into the pre-scaled query (1-2 heads) or the
 //   column factor and key zero term (3-8 heads).
 // * Online softmax in base 2 per 32-token block; heads live in MFMA rows, so
 //   each lane holds two heads' scores of one token and the row reductions
-//   are DPP moves inside a 16-lane row.
+//   are DPP moves inside a 16-lane row.  A block whose scores all stay at or
+//   below the running maxima (most blocks of a long cache) skips the
+//   reductions and the rescale; the sums are per lane until the end.
 // One wave per workgroup; a workgroup walks a range of 32-token blocks of
 // one slice (or that slice's residual) and either writes the normalised
 // output or, when the slice is split, its partial (max, sum, output) for a
@@ -223,7 +227,9 @@ struct alignas(16) Smem {
 };
 
 // Per-wave running softmax state and output accumulators for the two heads
-// this lane's MFMA rows hold (a = 2*kq, b = 2*kq + 1).
+// this lane's MFMA rows hold (a = 2*kq, b = 2*kq + 1).  The running maxima
+// are uniform over a 16-lane row; the sums l are this lane's share (its two
+// tokens of every block), summed over the row once at the end.
 template <int D>
 struct Acc {
     float m_a, m_b, l_a, l_b;
@@ -233,35 +239,50 @@ struct Acc {
 
 // Online-softmax update with scores x (log2 units) of two 16-token tiles;
 // returns the block weights p in xa/xb and rescales the accumulators.
-template <int D>
+// Where no score of the block exceeds its head's running maximum (all but a
+// few blocks of a long cache), the maximum stays and every rescale factor
+// is exactly 1, so the row reductions and the rescale are skipped; the
+// weights are the same either way.
+// HB: a lane row's second head can exist (at most one head per KV slice
+// leaves head b, and its weights, untouched).
+template <int D, bool HB>
 __device__ __forceinline__ void softmax_block(Acc<D>& acc, float xa[2], float xb[2]) {
-    const float bm_a = row16_max(fmaxf(xa[0], xa[1]));
-    const float bm_b = row16_max(fmaxf(xb[0], xb[1]));
-    const float mn_a = fmaxf(acc.m_a, bm_a), mn_b = fmaxf(acc.m_b, bm_b);
-    const float al_a = __builtin_amdgcn_exp2f(acc.m_a - mn_a);
-    const float al_b = __builtin_amdgcn_exp2f(acc.m_b - mn_b);
+    const float ma = fmaxf(xa[0], xa[1]), mb = HB ? fmaxf(xb[0], xb[1]) : kNegInf;
+    if (__ballot(ma > acc.m_a || (HB && mb > acc.m_b)) != 0) {
+        const float mn_a = fmaxf(acc.m_a, row16_max(ma));
+        const float al_a = __builtin_amdgcn_exp2f(acc.m_a - mn_a);
+        acc.m_a = mn_a;
+        acc.l_a *= al_a;
+        float al_b = 1.0f;
+        if constexpr (HB) {
+            const float mn_b = fmaxf(acc.m_b, row16_max(mb));
+            al_b = __builtin_amdgcn_exp2f(acc.m_b - mn_b);
+            acc.m_b = mn_b;
+            acc.l_b *= al_b;
+        }
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) {
+            acc.o[nt][0] *= al_a;
+            acc.o[nt][1] *= al_a;
+            if constexpr (HB) {
+                acc.o[nt][2] *= al_b;
+                acc.o[nt][3] *= al_b;
+            }
+        }
+        acc.z[0] *= al_a;
+        acc.z[1] *= al_a;
+        if constexpr (HB) {
+            acc.z[2] *= al_b;
+            acc.z[3] *= al_b;
+        }
+    }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-        xa[tt] = __builtin_amdgcn_exp2f(xa[tt] - mn_a);
-        xb[tt] = __builtin_amdgcn_exp2f(xb[tt] - mn_b);
+        xa[tt] = __builtin_amdgcn_exp2f(xa[tt] - acc.m_a);
+        if constexpr (HB) xb[tt] = __builtin_amdgcn_exp2f(xb[tt] - acc.m_b);
     }
-    acc.l_a = acc.l_a * al_a + row16_sum(xa[0] + xa[1]);
-    acc.l_b = acc.l_b * al_b + row16_sum(xb[0] + xb[1]);
-    acc.m_a = mn_a;
-    acc.m_b = mn_b;
-    // once the running maxima settle, alpha is exactly 1 everywhere: skip
-    if (__ballot(al_a != 1.0f || al_b != 1.0f) == 0) return;
-#pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) {
-        acc.o[nt][0] *= al_a;
-        acc.o[nt][1] *= al_a;
-        acc.o[nt][2] *= al_b;
-        acc.o[nt][3] *= al_b;
-    }
-    acc.z[0] *= al_a;
-    acc.z[1] *= al_a;
-    acc.z[2] *= al_b;
-    acc.z[3] *= al_b;
+    acc.l_a += xa[0] + xa[1];
+    if constexpr (HB) acc.l_b += xb[0] + xb[1];
 }
 
 // The residual block's softmax weights (this lane: tokens 16tt + j of heads
@@ -292,10 +313,12 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Acc<D>& ac
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
     const int r = a.q_per_kv;
     const int ha = 2 * kq, hb = 2 * kq + 1;
+    // the row totals of the lanes' partial sums
+    const float l_a = row16_sum(acc.l_a), l_b = row16_sum(acc.l_b);
     if (a.plan.n_splits == 1) {
         // a slice with no token at all (ragged batch) has l = 0: output 0
-        const float ia = acc.l_a > 0.0f ? 1.0f / acc.l_a : 0.0f;
-        const float ib = acc.l_b > 0.0f ? 1.0f / acc.l_b : 0.0f;
+        const float ia = l_a > 0.0f ? 1.0f / l_a : 0.0f;
+        const float ib = l_b > 0.0f ? 1.0f / l_b : 0.0f;
 #pragma unroll
         for (int nt = 0; nt < D / 16; ++nt) {
             if (ha < r) a.out[(s * r + ha) * D + 16 * nt + j] = __builtin_bit_cast(uint16_t, (f16)(oa[nt] * ia));
@@ -312,11 +335,11 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Acc<D>& ac
     if (j == 0) {
         if (ha < r) {
             a.ws_ml[(base + ha) * 2] = acc.m_a;
-            a.ws_ml[(base + ha) * 2 + 1] = acc.l_a;
+            a.ws_ml[(base + ha) * 2 + 1] = l_a;
         }
         if (hb < r) {
             a.ws_ml[(base + hb) * 2] = acc.m_b;
-            a.ws_ml[(base + hb) * 2 + 1] = acc.l_b;
+            a.ws_ml[(base + hb) * 2 + 1] = l_b;
         }
     }
 }
@@ -325,13 +348,22 @@ __device__ __forceinline__ void write_result(const AttnArgs& a, const Acc<D>& ac
 // the attention kernel: blockIdx.x = slice * n_splits + split
 // ---------------------------------------------------------------------------
 
-// Register budget for 3 waves per SIMD where the compiler can meet it
-// (measured 5% faster than 2 at head_dim 128, 2/2-bit); the wider code
-// types stay at 2, which the compiler reports and this file accepts.
+// Register budget: 4 waves per SIMD (128 VGPRs) for the one-head variant
+// with codes of at most 4 bits and the two-head one with 2-bit values,
+// which fit it without spilling; 3 waves for the rest where the compiler
+// can meet it (measured 5% faster than 2 at head_dim 128, 2/2-bit); the
+// wider code types stay at 2, which the compiler reports and this file
+// accepts.
+template <int KB, int VB, int RMAX>
+constexpr int min_waves() {
+    return (RMAX == 1 && KB <= 4 && VB <= 4) || (RMAX == 2 && KB <= 4 && VB == 2) ? 4 : 3;
+}
 #pragma clang diagnostic ignored "-Wpass-failed"
 template <int KB, int VB, int D, int G, int RMAX>
-__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8))) attention_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_waves<KB, VB, RMAX>(), 8))) attention_kernel(const AttnArgs a) {
     constexpr int NK32 = D / 32, NT16 = D / 16, ROWS = 2 * RMAX, OROWS = operand_rows<RMAX>();
+    constexpr bool HB = RMAX > 1;                         // a lane row can hold a second head
+    constexpr bool FEW = RMAX <= 2;                       // at most two heads: all in lane row 0
     __shared__ Smem<KB, VB, D, RMAX> sm;
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
     const int r = a.q_per_kv;
@@ -358,6 +390,9 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     // A-operand rows: lane row j; lanes of rows >= ROWS read the zero row
     // (there are none when ROWS = 16)
     const int jr = j < ROWS ? j : OROWS - 1;
+    // key-score A rows: with at most two heads their rows repeat in every
+    // group of four, so every lane row gets the scores of all heads
+    const int jk = FEW ? ((j & 3) < ROWS ? (j & 3) : OROWS - 1) : jr;
     // q as MFMA A operand, rows 2h = q_h and 2h+1 = 0: lane row j, channels
     // 32*kk + 8*kq .. +7
     const int qr = ((j & 1) == 0 && (j >> 1) < RMAX) ? j >> 1 : RMAX;
@@ -396,9 +431,9 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
 #pragma unroll
                 for (int kk = 0; kk < NK32; ++kk) sc = mfma(qa(kk), __builtin_bit_cast(h8, w[kk]), sc);
                 xa[tt] = valid ? (sc[0] + sc[1]) * a.logit_scale : kNegInf;
-                xb[tt] = valid ? (sc[2] + sc[3]) * a.logit_scale : kNegInf;
+                xb[tt] = HB && valid ? (sc[2] + sc[3]) * a.logit_scale : kNegInf;
             }
-            softmax_block(acc, xa, xb);
+            softmax_block<D, HB>(acc, xa, xb);
             weights_to_lds(sm, xa, xb, r);
             // values: B[token 8kq+e][channel 16nt+j]
             const h8 pa8 = lds_h8(&sm.apz[jr][8 * kq]);
@@ -456,9 +491,9 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     // would accumulate it) instead of four MFMAs and their LDS operands.
     float qreg[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
     float zg0 = 0.0f, zg1 = 0.0f;                         // zero terms of heads 0 and 1
-    if constexpr (RMAX == 2) {
+    if constexpr (FEW) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < RMAX; ++h)
             if (h < r && pair_live) {
                 const uint32_t qw = *reinterpret_cast<const uint32_t*>(a.q + (s * r + h) * D + 2 * L);
                 qreg[h][0] = lo_f(qw) * a.logit_scale;
@@ -556,15 +591,15 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             }
         }
         // a new key group: q*s operand rows (fp32 product split hi/lo) and zeros
-        if constexpr (RMAX == 2) {
+        if constexpr (FEW) {
             if (t0 % G == 0 || blk == b0) {
                 const float z0 = pair_live ? lo_f(st.kz) : 0.0f, z1 = pair_live ? hi_f(st.kz) : 0.0f;
                 zg0 = wave_sum(__builtin_fmaf(qreg[0][1], z1, qreg[0][0] * z0));
-                zg1 = r > 1 ? wave_sum(__builtin_fmaf(qreg[1][1], z1, qreg[1][0] * z0)) : 0.0f;
+                if constexpr (HB) zg1 = r > 1 ? wave_sum(__builtin_fmaf(qreg[1][1], z1, qreg[1][0] * z0)) : 0.0f;
                 if (pair_live) {
                     const float s0 = lo_f(st.ks), s1 = hi_f(st.ks);
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int h = 0; h < RMAX; ++h) {
                         if (h < r) {
                             uint32_t hi, lo;
                             split_prod2(qreg[h][0], s0, qreg[h][1], s1, hi, lo);
@@ -591,13 +626,13 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
     const CodePos<KB> kpos(j % (32 / KB));
     const CodePos<VB> vpos(j % (32 / VB));
     // the logit scale rides on the column factor where q is not pre-scaled
-    const float kcol = RMAX == 2 ? kpos.col : kpos.col * a.logit_scale;
+    const float kcol = FEW ? kpos.col : kpos.col * a.logit_scale;
     const int zrow = j < ngv ? j : 4;                     // value-zero operand row (4: zeros)
     f4 zk = f4{0, 0, 0, 0};
     Stage stage;
     // blocks [b0, bf) hold 32 valid tokens each; only the slice's last block
     // may be partial and needs the per-token bounds
-    const int bf = RMAX == 2 ? b0 : min(b1, n / 32);
+    const int bf = min(b1, n / 32);
     if (b0 < bf) load(b0, stage, std::true_type{});
     else if (b0 < b1) load(b0, stage, std::false_type{});
 
@@ -611,7 +646,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
 
         // keys: the zero-point term of a new group, then the scores of two
         // 16-token tiles
-        if (RMAX != 2 && (t0 % G == 0 || blk == b0)) {
+        if (!FEW && (t0 % G == 0 || blk == b0)) {
             zk = f4{0, 0, 0, 0};
 #pragma unroll
             for (int kk = 0; kk < NK32; ++kk) zk = mfma(qa(kk), lds_h8(&sm.kz[32 * kk + 8 * kq]), zk);
@@ -619,7 +654,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
         f4 sc[2] = {f4{0, 0, 0, 0}, f4{0, 0, 0, 0}};
 #pragma unroll
         for (int kk = 0; kk < NK32; ++kk) {
-            const h8 aop = lds_h8(&sm.aq[jr][32 * kk + 8 * kq]);
+            const h8 aop = lds_h8(&sm.aq[jk][32 * kk + 8 * kq]);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int wi = (16 * tt + j) / (32 / KB);
@@ -629,14 +664,14 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             }
         }
         float xa[2], xb[2];
-        const float za = RMAX == 2 ? zg0 : zk[0] * a.logit_scale, zb = RMAX == 2 ? zg1 : zk[2] * a.logit_scale;
+        const float za = FEW ? zg0 : zk[0] * a.logit_scale, zb = FEW ? zg1 : zk[2] * a.logit_scale;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const bool valid = FULL || t0 + 16 * tt + j < n;
             xa[tt] = valid ? (sc[tt][0] + sc[tt][1]) * kcol + za : kNegInf;
-            xb[tt] = valid ? (sc[tt][2] + sc[tt][3]) * kcol + zb : kNegInf;
+            xb[tt] = HB && valid ? (sc[tt][2] + sc[tt][3]) * kcol + zb : kNegInf;
         }
-        softmax_block(acc, xa, xb);
+        softmax_block<D, HB>(acc, xa, xb);
 
         // values: the product runs over the block's tokens in the slot
         // order of vslot (tokens t and t + 16 in adjacent slots), so the two
@@ -679,19 +714,13 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
                     }
                 }
             }
-        } else if constexpr (RMAX == 2 && NGV >= 2) {
-            // the heads live in lane row kq = 0; row kq takes value groups
-            // kq, kq + 4, ... of both heads (weights copied from lane j)
-            float ya[2], yb[2];
+        } else if constexpr (FEW && NGV >= 2) {
+            // every lane row holds the weights of both heads (the key-score
+            // rows repeat); row kq takes value groups kq, kq + 4, ...
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                ya[tt] = __shfl(xa[tt], j, kWave);
-                yb[tt] = r > 1 ? __shfl(xb[tt], j, kWave) : 0.0f;
-            }
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+            for (int hh = 0; hh < RMAX; ++hh) {
                 if (hh < r) {
-                    const float p0 = hh ? yb[0] : ya[0], p1 = hh ? yb[1] : ya[1];
+                    const float p0 = hh ? xb[0] : xa[0], p1 = hh ? xb[1] : xa[1];
                     uint32_t hi, lo;
                     if (kq == 0) {
                         split_prod2(p0, 1.0f, p1, 1.0f, hi, lo);
@@ -711,7 +740,7 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3, 8
             }
         } else {
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+            for (int hh = 0; hh < (HB ? 2 : 1); ++hh) {
                 const int h = 2 * kq + hh;
                 if (h < r) {
                     const float p0 = hh ? xb[0] : xa[0], p1 = hh ? xb[1] : xa[1];
@@ -796,7 +825,9 @@ __global__ void __launch_bounds__(kWave) attention_merge_kernel(const AttnArgs a
 template <int KB, int VB, int D, int G>
 int run_attention(const AttnArgs& a, hipStream_t st) {
     const int64_t groups = a.n_slices * a.plan.n_splits;
-    if (a.q_per_kv <= 2)
+    if (a.q_per_kv <= 1)
+        hipLaunchKernelGGL((attention_kernel<KB, VB, D, G, 1>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
+    else if (a.q_per_kv <= 2)
         hipLaunchKernelGGL((attention_kernel<KB, VB, D, G, 2>), dim3((unsigned)groups), dim3(kWave), 0, st, a);
     else if (a.q_per_kv <= 4)
         hipLaunchKernelGGL((attention_kernel<KB, VB, D, G, 4>), dim3((unsigned)groups), dim3(kWave), 0, st, a);

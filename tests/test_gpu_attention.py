@@ -146,6 +146,12 @@ def test_bit_combinations(kb, vb):
     run_case(kb, vb, 32, 128, 4, n=1000, n_res=100, seed=kb * 10 + vb)
 
 
+@pytest.mark.parametrize("kb,vb", BITS)
+def test_bit_combinations_one_head(kb, vb):
+    # the one-head variant (its register budget depends on the code widths)
+    run_case(kb, vb, 32, 128, 1, n=1000, n_res=100, seed=kb * 10 + vb + 100)
+
+
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("D", [32, 64, 96, 128])
 @pytest.mark.parametrize("r", [1, 8])
@@ -198,9 +204,10 @@ def test_zero_query_is_the_mean_of_all_values():
 def test_grouped_heads_match_smaller_groups_bitwise():
     """A head's result does not depend on which other heads share the call,
     within one zero-point formulation: with 1-2 heads per KV slice the key
-    zero-point term is a wave reduction, with 3-8 an MFMA product (kernel
-    variants for at most 4 and at most 8 heads share that arithmetic); the
-    two formulations differ only in that sum's order."""
+    zero-point term is a wave reduction, with 3-8 an MFMA product (the
+    kernel variants for at most 1 and at most 2 heads share one of these
+    arithmetics, those for at most 4 and at most 8 the other); the two
+    formulations differ only in that sum's order."""
     S, n, n_res, D = 3, 700, 40, 128
     k, v, q = _gen(99, S, n, n_res, D, 4)
     got2, _ = run_case(2, 4, 32, D, 2, n, n_res, q=q[:, :2], k=k, v=v)
