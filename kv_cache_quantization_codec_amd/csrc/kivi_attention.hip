@@ -390,12 +390,15 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
     // A-operand rows: lane row j; lanes of rows >= ROWS read the zero row
     // (there are none when ROWS = 16)
     const int jr = j < ROWS ? j : OROWS - 1;
-    // key-score A rows: with at most two heads their rows repeat in every
-    // group of four, so every lane row gets the scores of all heads
-    const int jk = FEW ? ((j & 3) < ROWS ? (j & 3) : OROWS - 1) : jr;
-    // q as MFMA A operand, rows 2h = q_h and 2h+1 = 0: lane row j, channels
-    // 32*kk + 8*kq .. +7
-    const int qr = ((j & 1) == 0 && (j >> 1) < RMAX) ? j >> 1 : RMAX;
+    // key-score A rows: with at most 2 (4) heads their rows repeat in every
+    // group of 4 (8) MFMA rows, so every lane row gets the scores of the
+    // heads whose weights it works on
+    constexpr int PER = FEW ? 4 : RMAX == 4 ? 8 : 16;
+    const int jp = j % PER;
+    const int jk = jp < ROWS ? jp : OROWS - 1;
+    // q as MFMA A operand, rows 2h = q_h and 2h+1 = 0 (repeating like the
+    // key-score rows): lane row j, channels 32*kk + 8*kq .. +7
+    const int qr = ((jp & 1) == 0 && (jp >> 1) < RMAX) ? jp >> 1 : RMAX;
     auto qa = [&](int kk) { return lds_h8(&sm.q[qr][32 * kk + 8 * kq]); };
 
     Acc<D> acc;
@@ -507,10 +510,15 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
     constexpr int KV = (KCH + kWave - 1) / kWave;
     constexpr int VU = 8 * RW;                            // value units: one word column of 4 tokens
     constexpr int VV = (VU + kWave - 1) / kWave;
+    // value scales and zeros of a block: 32 rows of NGV halves, staged as
+    // pairs of one row (a dword) when NGV is even, else one half per load
+    constexpr int SPL = NGV % 2 == 0 ? 2 : 1;             // halves per staged load
+    constexpr int NSE = 32 * NGV / SPL;                   // staged loads per block
+    constexpr int NSW = (NSE + kWave - 1) / kWave;
     struct Stage {
         u32x4 k[KV];
         uint32_t v[VV][4];
-        uint16_t vsb[(32 * NGV + kWave - 1) / kWave], vzb[(32 * NGV + kWave - 1) / kWave];
+        uint32_t vsb[NSW], vzb[NSW];
         uint32_t ks, kz;
     };
     // Addresses: wave-uniform bases of the block (64-bit, scalar) plus lane
@@ -546,13 +554,18 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
             }
         }
 #pragma unroll
-        for (int i = 0; i < (32 * NGV + kWave - 1) / kWave; ++i) {
-            const int e = L + kWave * i;
-            if (32 * NGV % kWave == 0 || e < 32 * NGV) {
+        for (int i = 0; i < NSW; ++i) {
+            const int e = SPL * (L + kWave * i);
+            if (NSE % kWave == 0 || e < 32 * NGV) {
                 const int row = e / NGV, gv = e - row * NGV;
                 const uint32_t off = 2u * (uint32_t)(clamp(row) * NGV + gv);   // masked below
-                st.vsb[i] = *at_byte(srow, off);
-                st.vzb[i] = *at_byte(zrow, off);
+                if constexpr (SPL == 2) {    // 4-byte aligned: even NGV and gv
+                    st.vsb[i] = *at_byte(reinterpret_cast<const uint32_t*>(srow), off);
+                    st.vzb[i] = *at_byte(reinterpret_cast<const uint32_t*>(zrow), off);
+                } else {
+                    st.vsb[i] = *at_byte(srow, off);
+                    st.vzb[i] = *at_byte(zrow, off);
+                }
             }
         }
         if ((t0 % G == 0 || blk == b0) && pair_live) {
@@ -581,13 +594,18 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
             }
         }
 #pragma unroll
-        for (int i = 0; i < (32 * NGV + kWave - 1) / kWave; ++i) {
-            const int e = L + kWave * i;
-            if (32 * NGV % kWave == 0 || e < 32 * NGV) {
+        for (int i = 0; i < NSW; ++i) {
+            const int e = SPL * (L + kWave * i);
+            if (NSE % kWave == 0 || e < 32 * NGV) {
                 const int row = e / NGV, gv = e - row * NGV;
                 const bool live = FULL || t0 + row < n;
-                sm.vs[gv][row] = live ? (float)__builtin_bit_cast(f16, st.vsb[i]) : 0.0f;
-                sm.vz[gv][vslot(row & 15) + (row >> 4)] = __builtin_bit_cast(f16, live ? st.vzb[i] : (uint16_t)0);
+                const int zs = vslot(row & 15) + (row >> 4);
+#pragma unroll
+                for (int u = 0; u < SPL; ++u) {
+                    const uint16_t sb = (uint16_t)(st.vsb[i] >> (16 * u)), zb = (uint16_t)(st.vzb[i] >> (16 * u));
+                    sm.vs[gv + u][row] = live ? (float)__builtin_bit_cast(f16, sb) : 0.0f;
+                    sm.vz[gv + u][zs] = __builtin_bit_cast(f16, live ? zb : (uint16_t)0);
+                }
             }
         }
         // a new key group: q*s operand rows (fp32 product split hi/lo) and zeros
@@ -680,23 +698,16 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
         // every value group.  Lane rows that hold no head take a share of
         // the groups, with the weights copied from the lanes that hold them.
         if constexpr (RMAX == 4 && NGV >= 2) {
-            // heads live in lane rows kq = 0, 1; rows 2, 3 take the upper half
-            // of the value groups of the heads of row kq - 2 (their weights
-            // copied from lane L ^ 32)
-            float ya[2], yb[2];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                ya[tt] = __shfl_xor(xa[tt], 32, kWave);
-                yb[tt] = __shfl_xor(xb[tt], 32, kWave);
-            }
+            // heads live in lane rows kq = 0, 1; rows 2, 3 repeat them (the
+            // key-score rows repeat) and take the upper half of the value
+            // groups
             const bool upper = kq >= 2;
             constexpr int HG = NGV / 2;                    // groups of the lower rows
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const int h = 2 * (kq & 1) + hh;
                 if (h < r) {
-                    const float p0 = upper ? (hh ? yb[0] : ya[0]) : (hh ? xb[0] : xa[0]);
-                    const float p1 = upper ? (hh ? yb[1] : ya[1]) : (hh ? xb[1] : xa[1]);
+                    const float p0 = hh ? xb[0] : xa[0], p1 = hh ? xb[1] : xa[1];
                     uint32_t hi, lo;
                     if (!upper) {
                         split_prod2(p0, 1.0f, p1, 1.0f, hi, lo);
