@@ -503,6 +503,18 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
                 qreg[h][1] = hi_f(qw) * a.logit_scale;
             }
     }
+    // Three or four heads: their query channels (2L, 2L+1) stay in
+    // registers too (unscaled), for the q*s operand rows of each key group.
+    float q4[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+    if constexpr (RMAX == 4) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+            if (h < r && pair_live) {
+                const uint32_t qw = *reinterpret_cast<const uint32_t*>(a.q + (s * r + h) * D + 2 * L);
+                q4[h][0] = lo_f(qw);
+                q4[h][1] = hi_f(qw);
+            }
+    }
 
     // One block's global data, held in registers from the previous block's
     // compute until it is written to LDS (so its load latency is hidden).
@@ -630,12 +642,24 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
         } else if ((t0 % G == 0 || blk == b0) && pair_live) {
             const float s0 = lo_f(st.ks), s1 = hi_f(st.ks);
             *reinterpret_cast<uint32_t*>(&sm.kz[2 * L]) = st.kz;
-            for (int h = 0; h < r; ++h) {
-                const uint32_t qw = *reinterpret_cast<const uint32_t*>(&sm.q[h][2 * L]);
-                uint32_t hi, lo;
-                split_prod2(lo_f(qw), s0, hi_f(qw), s1, hi, lo);
-                *reinterpret_cast<uint32_t*>(&sm.aq[2 * h][2 * L]) = hi;
-                *reinterpret_cast<uint32_t*>(&sm.aq[2 * h + 1][2 * L]) = lo;
+            if constexpr (RMAX == 4) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    if (h < r) {
+                        uint32_t hi, lo;
+                        split_prod2(q4[h][0], s0, q4[h][1], s1, hi, lo);
+                        *reinterpret_cast<uint32_t*>(&sm.aq[2 * h][2 * L]) = hi;
+                        *reinterpret_cast<uint32_t*>(&sm.aq[2 * h + 1][2 * L]) = lo;
+                    }
+                }
+            } else {
+                for (int h = 0; h < r; ++h) {
+                    const uint32_t qw = *reinterpret_cast<const uint32_t*>(&sm.q[h][2 * L]);
+                    uint32_t hi, lo;
+                    split_prod2(lo_f(qw), s0, hi_f(qw), s1, hi, lo);
+                    *reinterpret_cast<uint32_t*>(&sm.aq[2 * h][2 * L]) = hi;
+                    *reinterpret_cast<uint32_t*>(&sm.aq[2 * h + 1][2 * L]) = lo;
+                }
             }
         }
     };
