@@ -375,18 +375,25 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
     const int n_quant_s = a.n_quant_s ? min(max(a.n_quant_s[s], 0), a.n_quant) : a.n_quant;
     const int res_count_s = a.res_count_s ? min(max(a.res_count_s[s], 0), a.res_count) : a.res_count;
 
-    // operand rows that are never written (and the zero rows) stay zero
-    for (int i = L; i < OROWS * (D + 8); i += kWave) (&sm.aq[0][0])[i] = (f16)0;
-    for (int i = L; i < 4 * OROWS * kTokStride; i += kWave) (&sm.ap[0][0][0])[i] = (f16)0;
-    for (int i = L; i < OROWS * kTokStride; i += kWave) (&sm.apz[0][0])[i] = (f16)0;
-    if (L < kTokStride) sm.vz[4][L] = (f16)0;
-    // the queries to LDS; rows of heads >= r and the zero row are zero
-    for (int i = L; i < (RMAX + 1) * D / 8; i += kWave) {
-        const int h = i / (D / 8), c = 8 * (i - h * (D / 8));
-        u32x4 w = u32x4{0, 0, 0, 0};
-        if (h < r && h < RMAX) w = *reinterpret_cast<const u32x4*>(a.q + (s * r + h) * D + c);
-        *reinterpret_cast<u32x4*>(&sm.q[h][c]) = w;
-    }
+    // LDS set-up: operand rows that are never written (and the zero rows)
+    // stay zero; the queries, where the kernel reads them from LDS (rows of
+    // heads >= r and the zero row are zero).  One wave per workgroup: its
+    // LDS accesses execute in order, so a compiler barrier orders them (a
+    // __syncthreads fence would also wait for every load in flight).
+    auto setup_lds = [&](bool with_q) {
+        for (int i = L; i < OROWS * (D + 8); i += kWave) (&sm.aq[0][0])[i] = (f16)0;
+        for (int i = L; i < 4 * OROWS * kTokStride; i += kWave) (&sm.ap[0][0][0])[i] = (f16)0;
+        for (int i = L; i < OROWS * kTokStride; i += kWave) (&sm.apz[0][0])[i] = (f16)0;
+        if (L < kTokStride) sm.vz[4][L] = (f16)0;
+        if (with_q)
+            for (int i = L; i < (RMAX + 1) * D / 8; i += kWave) {
+                const int h = i / (D / 8), c = 8 * (i - h * (D / 8));
+                u32x4 w = u32x4{0, 0, 0, 0};
+                if (h < r && h < RMAX) w = *reinterpret_cast<const u32x4*>(a.q + (s * r + h) * D + c);
+                *reinterpret_cast<u32x4*>(&sm.q[h][c]) = w;
+            }
+        lds_order();
+    };
     // A-operand rows: lane row j; lanes of rows >= ROWS read the zero row
     // (there are none when ROWS = 16)
     const int jr = j < ROWS ? j : OROWS - 1;
@@ -407,12 +414,12 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
 #pragma unroll
     for (int nt = 0; nt < NT16; ++nt) acc.o[nt] = f4{0, 0, 0, 0};
     acc.z = f4{0, 0, 0, 0};
-    __syncthreads();
 
     float oa[NT16], ob[NT16];
 
     if (residual) {
         // ---- fp16 residual: plain fp16 operands ----
+        setup_lds(true);
         const uint16_t* rk = a.res_k + s * a.res_stride;
         const uint16_t* rv = a.res_v + s * a.res_stride;
         for (int i0 = 0; i0 < res_count_s; i0 += 32) {
@@ -675,8 +682,13 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
     // blocks [b0, bf) hold 32 valid tokens each; only the slice's last block
     // may be partial and needs the per-token bounds
     const int bf = min(b1, n / 32);
+    // with 1-2 heads the quantized prefix reads no query from LDS (the
+    // query registers above serve it), so its LDS set-up follows the first
+    // block's loads; with 3-8 heads the query rows go first
+    if constexpr (!FEW) setup_lds(true);
     if (b0 < bf) load(b0, stage, std::true_type{});
     else if (b0 < b1) load(b0, stage, std::false_type{});
+    if constexpr (FEW) setup_lds(false);
 
     auto block = [&](int blk, auto full_tag) {
         constexpr bool FULL = decltype(full_tag)::value;
