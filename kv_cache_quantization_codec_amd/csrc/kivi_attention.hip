@@ -840,33 +840,60 @@ __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_
     write_result<D>(a, acc, s, split, oa, ob);
 }
 
-// Merge of the partial results of a split slice: one workgroup per (slice,
-// query head), lanes over channels.
-__global__ void __launch_bounds__(kWave) attention_merge_kernel(const AttnArgs a) {
+// Merge of the partial results of a split slice: one wave per (slice,
+// query head), four of them per workgroup, lanes over channels.  The
+// splits' loads go out four at a time; the sums run over the splits in
+// order.
+constexpr int kMergeWaves = 4;
+__global__ void __launch_bounds__(kMergeWaves * kWave) attention_merge_kernel(const AttnArgs a) {
     const int r = a.q_per_kv, D = a.head_dim, ns = a.plan.n_splits;
-    const int64_t s = blockIdx.x / r;
-    const int h = (int)(blockIdx.x - s * r);
-    const int L = threadIdx.x;
+    const int64_t pair = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+    if (pair >= a.n_slices * r) return;
+    const int64_t s = pair / r;
+    const int h = (int)(pair - s * r);
+    const int L = threadIdx.x & (kWave - 1);
+    const bool c0 = L < D, c1 = L + kWave < D;
+    const int64_t base0 = s * ns * r + h;                 // partial of split i: base0 + i * r
     float mx = kNegInf;
-    for (int i = 0; i < ns; ++i) mx = fmaxf(mx, a.ws_ml[((s * ns + i) * r + h) * 2]);
+    for (int i0 = 0; i0 < ns; i0 += 4) {
+        float m[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m[u] = i0 + u < ns ? a.ws_ml[(base0 + (int64_t)(i0 + u) * r) * 2] : kNegInf;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mx = fmaxf(mx, m[u]);
+    }
+    uint16_t* dst = a.out + (s * r + h) * D;
     if (mx == kNegInf) {                       // a slice with no token at all: output 0
-        uint16_t* dst = a.out + (s * r + h) * D;
-        if (L < D) dst[L] = 0;
-        if (L + kWave < D) dst[L + kWave] = 0;
+        if (c0) dst[L] = 0;
+        if (c1) dst[L + kWave] = 0;
         return;
     }
     float lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int i = 0; i < ns; ++i) {
-        const int64_t base = (s * ns + i) * r + h;
-        const float w = __builtin_amdgcn_exp2f(a.ws_ml[base * 2] - mx);
-        lsum += w * a.ws_ml[base * 2 + 1];
-        if (L < D) o0 += w * a.ws_o[base * D + L];
-        if (L + kWave < D) o1 += w * a.ws_o[base * D + L + kWave];
+    for (int i0 = 0; i0 < ns; i0 += 4) {
+        float mm[4], ll[4], x0[4], x1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool in = i0 + u < ns;
+            const int64_t b = base0 + (int64_t)(in ? i0 + u : 0) * r;
+            mm[u] = a.ws_ml[b * 2];
+            ll[u] = a.ws_ml[b * 2 + 1];
+            x0[u] = c0 ? a.ws_o[b * D + L] : 0.0f;
+            x1[u] = c1 ? a.ws_o[b * D + L + kWave] : 0.0f;
+            if (!in) mm[u] = kNegInf;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (i0 + u < ns) {
+                const float w = __builtin_amdgcn_exp2f(mm[u] - mx);
+                lsum += w * ll[u];
+                o0 += w * x0[u];
+                o1 += w * x1[u];
+            }
+        }
     }
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;   // a slice with no token: 0
-    uint16_t* dst = a.out + (s * r + h) * D;
-    if (L < D) dst[L] = __builtin_bit_cast(uint16_t, (f16)(o0 * inv));
-    if (L + kWave < D) dst[L + kWave] = __builtin_bit_cast(uint16_t, (f16)(o1 * inv));
+    if (c0) dst[L] = __builtin_bit_cast(uint16_t, (f16)(o0 * inv));
+    if (c1) dst[L + kWave] = __builtin_bit_cast(uint16_t, (f16)(o1 * inv));
 }
 
 template <int KB, int VB, int D, int G>
@@ -883,8 +910,9 @@ int run_attention(const AttnArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     if (a.plan.n_splits > 1) {
-        hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)(a.n_slices * a.q_per_kv)), dim3(kWave), 0,
-                           st, a);
+        const int64_t pairs = a.n_slices * a.q_per_kv;
+        hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)((pairs + kMergeWaves - 1) / kMergeWaves)),
+                           dim3(kMergeWaves * kWave), 0, st, a);
         e = hipGetLastError();
     }
     return (int)e;
