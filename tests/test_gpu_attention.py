@@ -320,10 +320,12 @@ def run_ragged(kb, vb, G, D, r, n_list, res_list, *, seed, cap=None, slots=None,
     return got
 
 
-def test_ragged_split_path():
-    # few slices and a long bound: the split plan and the merge kernel
-    run_ragged(2, 2, 32, 128, 4, [0, 1, 33, 700, 2000, 2047, 64, 0],
-               [0, 0, 5, 128, 0, 77, 128, 9], seed=21, slots=160, head=150)
+@pytest.mark.parametrize("r", [1, 4])
+def test_ragged_split_path(r):
+    # few slices and a long bound: the split plan and the merge kernel (the
+    # one-head and the 4-head variants)
+    run_ragged(2, 2, 32, 128, r, [0, 1, 33, 700, 2000, 2047, 64, 0],
+               [0, 0, 5, 128, 0, 77, 128, 9], seed=21 + r, slots=160, head=150)
 
 
 @pytest.mark.parametrize("part", ["quantized", "residual"])
