@@ -36,10 +36,11 @@
 // * Four kernel variants by the bound on query heads per KV slice (1, 2,
 //   4, 8) size the LDS operand rows and drop the second head of a lane row
 //   where there is none.  Lane rows of the value-weight step that hold no
-//   head take a share of the value groups; with 1-2 heads the key-score
-//   operand rows repeat in every group of four MFMA rows, so every lane row
-//   has the weights without a cross-lane copy.  A slice's full 32-token
-//   blocks run without per-token bounds; only its last block can be partial.
+//   head take a share of the value groups; the key-score operand rows
+//   repeat in every group of four (1-2 heads) or eight (3-4 heads) MFMA
+//   rows, so every lane row has the weights it needs without a cross-lane
+//   copy.  A slice's full 32-token blocks run without per-token bounds;
+//   only its last block can be partial.
 // * The logit scale is folded into the pre-scaled query (1-2 heads) or the
 //   column factor and key zero term (3-8 heads).
 // * Online softmax in base 2 per 32-token block; heads live in MFMA rows, so
