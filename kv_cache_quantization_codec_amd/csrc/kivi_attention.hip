@@ -364,7 +364,7 @@ template <int KB, int VB, int D, int G, int RMAX>
 __global__ void __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(min_waves<KB, VB, RMAX>(), 8))) attention_kernel(const AttnArgs a) {
     constexpr int NK32 = D / 32, NT16 = D / 16, ROWS = 2 * RMAX, OROWS = operand_rows<RMAX>();
     constexpr bool HB = RMAX > 1;                         // a lane row can hold a second head
-    constexpr bool FEW = RMAX <= 2;                       // at most two heads: all in lane row 0
+    constexpr bool FEW = RMAX <= 2;                       // at most two heads: MFMA rows 0-3
     __shared__ Smem<KB, VB, D, RMAX> sm;
     const int L = threadIdx.x, j = L & 15, kq = L >> 4;
     const int r = a.q_per_kv;
